@@ -1,0 +1,213 @@
+"""Python binding of the expert-offload MoE layer step (C ABI in include/moe_offload.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libmoe_offload.so``.  Pointers are passed as integers (``tensor.data_ptr()``), streams
+as ``torch.cuda.Stream.cuda_stream`` integers (0 = null stream).  Importing this
+package fails loudly when the library has not been built (``python -m
+expert_cache_offload_amd.build`` or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_offload.so")
+
+MOE_OK, MOE_E_INVALID, MOE_E_CAPACITY, MOE_E_BUSY, MOE_E_HIP, MOE_E_NOMEM = 0, -1, -2, -3, -4, -5
+MOE_FMT_BF16, MOE_FMT_FP8_E4M3_K128, MOE_FMT_MXFP4_K32 = 0, 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m expert_cache_offload_amd.build)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("wfmt", ctypes.c_int32),
+                ("has_shared", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("blob_bytes", ctypes.c_int64)]
+
+
+class MoePlanHost(ctypes.Structure):
+    _fields_ = [("n_unique", ctypes.c_int32), ("n_hit", ctypes.c_int32),
+                ("n_miss", ctypes.c_int32), ("layer", ctypes.c_int32),
+                ("step", ctypes.c_int64),
+                ("unique", ctypes.c_void_p), ("slot", ctypes.c_void_p),
+                ("hit", ctypes.c_void_p), ("miss_key", ctypes.c_void_p),
+                ("miss_slot", ctypes.c_void_p), ("miss_victim", ctypes.c_void_p),
+                ("count", ctypes.c_void_p), ("perm", ctypes.c_void_p)]
+
+
+class MoeCounters(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("hits", ctypes.c_int64),
+                ("misses", ctypes.c_int64), ("bytes_filled", ctypes.c_int64)]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "moe_blob_bytes": (_i64, [_i32, _i32, _i32]),
+    "moe_workspace_bytes": (_sz, [ctypes.POINTER(MoeShape), _i32]),
+    "moe_host_pool_alloc": (_i32, [_sz, ctypes.POINTER(_vp)]),
+    "moe_host_pool_free": (_i32, [_vp]),
+    "moe_cache_create": (_i32, [ctypes.POINTER(MoeShape), _i32, _i32, _vp, _vp, _vp, _vp,
+                                ctypes.POINTER(_vp)]),
+    "moe_cache_destroy": (_i32, [_vp]),
+    "moe_cache_resize": (_i32, [_vp, _i32, _vp, _vp]),
+    "moe_route_classify": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "moe_fill_misses": (_i32, [_vp, _i32, _vp]),
+    "moe_expert_ffn": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "moe_layer_step": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
+    "moe_cache_snapshot": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_plan_read": (_i32, [_vp, ctypes.POINTER(MoePlanHost)]),
+    "moe_stats": (_i32, [_vp, ctypes.POINTER(MoeCounters)]),
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_last_hip_error": (_i32, [_vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, hip: int = 0):
+        msg = _lib.moe_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status}" + (f", hipError {hip})" if hip else ")"))
+        self.status = status
+
+
+def _check(st: int, where: str, handle=None) -> None:
+    if st != MOE_OK:
+        hip = _lib.moe_last_hip_error(handle) if handle else 0
+        raise MoeError(st, where, hip)
+
+
+def _p(x) -> int | None:
+    """Integer address of a tensor / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def make_shape(layers, experts, top_k, hidden, inter, wfmt, has_shared, max_tokens) -> MoeShape:
+    return MoeShape(layers, experts, top_k, hidden, inter, wfmt, int(has_shared), max_tokens,
+                    moe_blob_bytes(wfmt, hidden, inter))
+
+
+def moe_blob_bytes(wfmt: int, hidden: int, inter: int) -> int:
+    return int(_lib.moe_blob_bytes(wfmt, hidden, inter))
+
+
+def moe_workspace_bytes(shape: MoeShape, max_capacity: int) -> int:
+    return int(_lib.moe_workspace_bytes(ctypes.byref(shape), max_capacity))
+
+
+def moe_host_pool_alloc(nbytes: int) -> int:
+    out = _vp()
+    _check(_lib.moe_host_pool_alloc(nbytes, ctypes.byref(out)), "moe_host_pool_alloc")
+    return int(out.value)
+
+
+def moe_host_pool_free(addr: int) -> None:
+    _check(_lib.moe_host_pool_free(addr), "moe_host_pool_free")
+
+
+def moe_cache_create(shape: MoeShape, capacity: int, max_capacity: int, slot_arena, workspace,
+                     host_pool, stream: int = 0) -> int:
+    out = _vp()
+    st = _lib.moe_cache_create(ctypes.byref(shape), capacity, max_capacity, _p(slot_arena),
+                               _p(workspace), _p(host_pool), stream, ctypes.byref(out))
+    _check(st, "moe_cache_create")
+    return int(out.value)
+
+
+def moe_cache_destroy(handle: int) -> None:
+    _check(_lib.moe_cache_destroy(handle), "moe_cache_destroy")
+
+
+def moe_cache_resize(handle: int, new_capacity: int, new_arena=None, stream: int = 0) -> None:
+    _check(_lib.moe_cache_resize(handle, new_capacity, _p(new_arena), stream),
+           "moe_cache_resize", handle)
+
+
+def moe_route_classify(handle: int, layer: int, x, T: int, w_router, topk_idx=None, topk_w=None,
+                       stream: int = 0) -> None:
+    _check(_lib.moe_route_classify(handle, layer, _p(x), T, _p(w_router), _p(topk_idx),
+                                   _p(topk_w), stream), "moe_route_classify", handle)
+
+
+def moe_fill_misses(handle: int, groups: int = 2, fill_stream: int = 0) -> None:
+    _check(_lib.moe_fill_misses(handle, groups, fill_stream), "moe_fill_misses", handle)
+
+
+def moe_expert_ffn(handle: int, layer: int, x, T: int, shared_blob, y, stream: int = 0) -> None:
+    _check(_lib.moe_expert_ffn(handle, layer, _p(x), T, _p(shared_blob), _p(y), stream),
+           "moe_expert_ffn", handle)
+
+
+def moe_layer_step(handle: int, layer: int, x, T: int, w_router, shared_blob, y, topk_idx=None,
+                   topk_w=None, groups: int = 2, compute_stream: int = 0,
+                   fill_stream: int = 0) -> None:
+    _check(_lib.moe_layer_step(handle, layer, _p(x), T, _p(w_router), _p(shared_blob),
+                               _p(topk_idx), _p(topk_w), _p(y), groups, compute_stream,
+                               fill_stream), "moe_layer_step", handle)
+
+
+def moe_cache_snapshot(handle: int, capacity: int, n_keys: int):
+    """Returns (key_of, stamp, slot_of, n, step, capacity) as numpy arrays / ints."""
+    import numpy as np
+    key_of = np.empty(capacity, np.int32)
+    stamp = np.empty(capacity, np.int32)
+    slot_of = np.empty(n_keys, np.int32)
+    n = ctypes.c_int32()
+    step = ctypes.c_int64()
+    cap = ctypes.c_int32()
+    st = _lib.moe_cache_snapshot(handle, key_of.ctypes.data, stamp.ctypes.data,
+                                 slot_of.ctypes.data, ctypes.addressof(n),
+                                 ctypes.addressof(step), ctypes.addressof(cap))
+    _check(st, "moe_cache_snapshot", handle)
+    return key_of[:cap.value], stamp[:cap.value], slot_of, n.value, step.value, cap.value
+
+
+def moe_plan_read(handle: int, max_unique: int, max_assign: int) -> dict:
+    import numpy as np
+    bufs = {k: np.zeros(max_unique, np.int32) for k in
+            ("unique", "slot", "miss_key", "miss_slot", "miss_victim", "count")}
+    bufs["hit"] = np.zeros(max_unique, np.uint8)
+    bufs["perm"] = np.zeros(max(1, max_assign), np.int32)
+    ph = MoePlanHost(0, 0, 0, 0, 0, *[bufs[k].ctypes.data for k in
+                                      ("unique", "slot", "hit", "miss_key", "miss_slot",
+                                       "miss_victim", "count", "perm")])
+    _check(_lib.moe_plan_read(handle, ctypes.byref(ph)), "moe_plan_read", handle)
+    nu, nm = ph.n_unique, ph.n_miss
+    return {"n_unique": nu, "n_hit": ph.n_hit, "n_miss": nm, "layer": ph.layer, "step": ph.step,
+            "unique": bufs["unique"][:nu].copy(), "slot": bufs["slot"][:nu].copy(),
+            "hit": bufs["hit"][:nu].astype(bool), "miss_key": bufs["miss_key"][:nm].copy(),
+            "miss_slot": bufs["miss_slot"][:nm].copy(),
+            "miss_victim": bufs["miss_victim"][:nm].copy(), "count": bufs["count"][:nu].copy(),
+            "perm": bufs["perm"].copy()}
+
+
+def moe_stats(handle: int) -> dict:
+    c = MoeCounters()
+    _check(_lib.moe_stats(handle, ctypes.byref(c)), "moe_stats", handle)
+    return {"steps": c.steps, "hits": c.hits, "misses": c.misses, "bytes_filled": c.bytes_filled}
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_last_hip_error(handle: int) -> int:
+    return int(_lib.moe_last_hip_error(handle))
+
+
+__all__ = [n for n in _SIGS] + ["MoeShape", "MoePlanHost", "MoeCounters", "MoeError",
+                                "make_shape", "LIB_PATH"]

@@ -1,0 +1,459 @@
+// Host side of the C ABI declared in include/moe_offload.h: argument checks, workspace
+// layout, step orchestration across the compute and fill streams, resize and snapshots.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/moe_offload.h"
+#include "moe_dev.h"
+
+namespace moe {
+hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const void* wr,
+                             int* out_idx, float* out_w, int layer, int T, hipStream_t s);
+size_t route_plan_lds_bytes(const Dims& d);
+hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
+                             const void* shared_blob, int mode, int group, int ngroups, int T,
+                             int max_entries, hipStream_t s);
+size_t ffn_decode_lds_bytes(const Dims& d, int ntok);
+int decode_ntok(int T);
+hipError_t launch_combine(const Dims& d, const Dev& v, void* y, int T, int with_shared,
+                          hipStream_t s);
+hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
+                       int ngroups, int grid, hipStream_t s);
+hipError_t launch_init(const Dev& v, int max_capacity, int n_keys, int capacity, hipStream_t s);
+hipError_t launch_resize(const Dev& v, int new_capacity, int max_capacity, int E,
+                         const void* old_arena, void* new_arena, long long S, hipStream_t s);
+size_t resize_lds_bytes(int max_capacity);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxGroups = 64;
+constexpr int kMaxCapacity = 4096;  // LDS-resident LRU stamps and the resize sort
+constexpr int kFillGrid = 256;
+
+enum class State { Idle, Planned, Filled };
+
+struct Layout {
+  size_t key_of, stamp, slot_of, ctrl, stats, hdr, U, u_slot, u_hit, hit_list, miss_list,
+      miss_key, miss_slot, miss_victim, count, offset, perm, inv_pos, tk_idx, tk_w, logits,
+      partial, shared_partial, moves, total;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int rows_per_workgroup(int fmt, int inter) {
+  // R must divide the scale block of the down projection (128 for fp8, 32 for MXFP4).
+  int R = fmt == MOE_FMT_BF16 ? 16 : fmt == MOE_FMT_FP8_E4M3_K128 ? 64 : 32;
+  while (R > 1 && inter % R) R >>= 1;
+  return R;
+}
+
+Dims make_dims(const moe_shape& s, int max_capacity) {
+  Dims d{};
+  d.L = s.layers;
+  d.E = s.experts;
+  d.K = s.top_k;
+  d.H = s.hidden;
+  d.I = s.inter;
+  d.fmt = s.wfmt;
+  d.has_shared = s.has_shared;
+  d.max_tokens = s.max_tokens;
+  d.amax = s.max_tokens * s.top_k;
+  d.umax = d.amax < s.experts ? d.amax : s.experts;
+  d.max_capacity = max_capacity;
+  d.R = rows_per_workgroup(s.wfmt, s.inter);
+  d.nR = s.inter / d.R;
+  d.S = s.blob_bytes;
+  return d;
+}
+
+Layout make_layout(const Dims& d) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const size_t I4 = sizeof(int32_t);
+  L.key_of = take(I4 * d.max_capacity);
+  L.stamp = take(I4 * d.max_capacity);
+  L.slot_of = take(I4 * (size_t)d.L * d.E);
+  L.ctrl = take(I4 * CTRL_WORDS);
+  L.stats = take(sizeof(uint64_t) * STAT_WORDS);
+  L.hdr = take(I4 * HDR_WORDS);
+  L.U = take(I4 * d.umax);
+  L.u_slot = take(I4 * d.umax);
+  L.u_hit = take(I4 * d.umax);
+  L.hit_list = take(I4 * d.umax);
+  L.miss_list = take(I4 * d.umax);
+  L.miss_key = take(I4 * d.umax);
+  L.miss_slot = take(I4 * d.umax);
+  L.miss_victim = take(I4 * d.umax);
+  L.count = take(I4 * d.umax);
+  L.offset = take(I4 * (d.umax + 1));
+  L.perm = take(I4 * d.amax);
+  L.inv_pos = take(I4 * d.amax);
+  L.tk_idx = take(I4 * d.amax);
+  L.tk_w = take(sizeof(float) * d.amax);
+  L.logits = take(sizeof(double) * (size_t)d.max_tokens * d.E);
+  L.partial = take(sizeof(float) * (size_t)d.amax * d.nR * d.H);
+  L.shared_partial =
+      take(d.has_shared ? sizeof(float) * (size_t)d.max_tokens * d.nR * d.H : 256);
+  L.moves = take(I4 * 2 * (size_t)d.max_capacity);
+  L.total = o;
+  return L;
+}
+
+Dev make_dev(void* ws, const Layout& L) {
+  char* b = (char*)ws;
+  Dev v{};
+  v.key_of = (int*)(b + L.key_of);
+  v.stamp = (int*)(b + L.stamp);
+  v.slot_of = (int*)(b + L.slot_of);
+  v.ctrl = (int*)(b + L.ctrl);
+  v.stats = (unsigned long long*)(b + L.stats);
+  v.hdr = (int*)(b + L.hdr);
+  v.U = (int*)(b + L.U);
+  v.u_slot = (int*)(b + L.u_slot);
+  v.u_hit = (int*)(b + L.u_hit);
+  v.hit_list = (int*)(b + L.hit_list);
+  v.miss_list = (int*)(b + L.miss_list);
+  v.miss_key = (int*)(b + L.miss_key);
+  v.miss_slot = (int*)(b + L.miss_slot);
+  v.miss_victim = (int*)(b + L.miss_victim);
+  v.count = (int*)(b + L.count);
+  v.offset = (int*)(b + L.offset);
+  v.perm = (int*)(b + L.perm);
+  v.inv_pos = (int*)(b + L.inv_pos);
+  v.tk_idx = (int*)(b + L.tk_idx);
+  v.tk_w = (float*)(b + L.tk_w);
+  v.logits = (double*)(b + L.logits);
+  v.partial = (float*)(b + L.partial);
+  v.shared_partial = (float*)(b + L.shared_partial);
+  v.moves = (int*)(b + L.moves);
+  return v;
+}
+
+bool shape_ok(const moe_shape* s) {
+  if (!s) return false;
+  if (s->layers < 1 || s->experts < 1 || s->experts > 1024) return false;
+  if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->experts) return false;
+  if (s->hidden < 256 || s->hidden % 256) return false;
+  if (s->inter < 128 || s->inter % 128) return false;
+  if (s->wfmt < 0 || s->wfmt > 2) return false;
+  if (s->has_shared != 0 && s->has_shared != 1) return false;
+  if (s->max_tokens < 1 || s->max_tokens > kDecodeMaxTokens) return false;
+  if (s->blob_bytes != moe_blob_bytes(s->wfmt, s->hidden, s->inter)) return false;
+  if (s->blob_bytes % 16) return false;
+  if ((long long)s->layers * s->experts > (1ll << 30)) return false;
+  return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+struct moe_cache_s {
+  moe_shape shape;
+  Dims d;
+  Layout L;
+  Dev v;
+  int capacity;
+  int max_capacity;
+  int arena_slots;  // slots the current arena holds
+  void* arena;
+  void* workspace;
+  const void* host_pool;
+  const void* pool_dev;
+  hipEvent_t ev_plan;
+  hipEvent_t ev_fill[kMaxGroups];
+  State state;
+  int plan_T;
+  int plan_layer;
+  int fill_groups;
+  int last_hip;
+};
+
+static moe_status hip_fail(moe_cache c, hipError_t e) {
+  if (c) c->last_hip = (int)e;
+  return MOE_E_HIP;
+}
+
+extern "C" {
+
+int64_t moe_blob_bytes(int32_t wfmt, int32_t hidden, int32_t inter) {
+  const int64_t H = hidden, I = inter;
+  if (H <= 0 || I <= 0) return -1;
+  switch (wfmt) {
+    case MOE_FMT_BF16: return 6 * I * H;
+    case MOE_FMT_FP8_E4M3_K128:
+      if (H % 128 || I % 128) return -1;
+      return 3 * I * H + 4 * (2 * I * (H / 128)) + 4 * ((I / 128) * H);
+    case MOE_FMT_MXFP4_K32:
+      if (H % 64 || I % 32) return -1;
+      return 3 * I * H / 2 + 2 * I * (H / 32) + (I / 32) * H;
+    default: return -1;
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_capacity) {
+  if (!shape_ok(shape) || max_capacity < 1 || max_capacity > kMaxCapacity) return 0;
+  return make_layout(make_dims(*shape, max_capacity)).total;
+}
+
+moe_status moe_host_pool_alloc(size_t bytes, void** out) {
+  if (!out || bytes == 0) return MOE_E_INVALID;
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocNonCoherent);
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    *out = nullptr;
+    return MOE_E_NOMEM;
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+moe_status moe_host_pool_free(void* p) {
+  if (!p) return MOE_E_INVALID;
+  return hipHostFree(p) == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t max_capacity,
+                            void* slot_arena, void* workspace, const void* host_pool,
+                            void* stream, moe_cache* out) {
+  if (!out) return MOE_E_INVALID;
+  *out = nullptr;
+  if (!shape_ok(shape) || !slot_arena || !workspace || !host_pool) return MOE_E_INVALID;
+  if (!aligned16(slot_arena) || ((uintptr_t)workspace & 255)) return MOE_E_INVALID;
+  if (max_capacity < 1 || max_capacity > kMaxCapacity) return MOE_E_CAPACITY;
+  const int floor_c = shape->max_tokens * shape->top_k < shape->experts
+                          ? shape->max_tokens * shape->top_k
+                          : shape->experts;
+  if (capacity < floor_c || capacity > max_capacity) return MOE_E_CAPACITY;
+  void* pool_dev = nullptr;
+  if (hipHostGetDevicePointer(&pool_dev, const_cast<void*>(host_pool), 0) != hipSuccess ||
+      !pool_dev) {
+    (void)hipGetLastError();
+    return MOE_E_NOMEM;  // not pinned / not device-accessible
+  }
+  moe_cache c = new (std::nothrow) moe_cache_s();
+  if (!c) return MOE_E_NOMEM;
+  c->shape = *shape;
+  c->d = make_dims(*shape, max_capacity);
+  c->L = make_layout(c->d);
+  c->v = make_dev(workspace, c->L);
+  c->capacity = capacity;
+  c->max_capacity = max_capacity;
+  c->arena_slots = max_capacity;
+  c->arena = slot_arena;
+  c->workspace = workspace;
+  c->host_pool = host_pool;
+  c->pool_dev = pool_dev;
+  c->state = State::Idle;
+  hipError_t e = hipEventCreateWithFlags(&c->ev_plan, hipEventDisableTiming);
+  for (int g = 0; g < kMaxGroups && e == hipSuccess; ++g)
+    e = hipEventCreateWithFlags(&c->ev_fill[g], hipEventDisableTiming);
+  if (e == hipSuccess)
+    e = launch_init(c->v, max_capacity, shape->layers * shape->experts, capacity,
+                    (hipStream_t)stream);
+  if (e != hipSuccess) {
+    moe_cache_destroy(c);
+    return MOE_E_HIP;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_destroy(moe_cache c) {
+  if (!c) return MOE_E_INVALID;
+  if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
+  for (int g = 0; g < kMaxGroups; ++g)
+    if (c->ev_fill[g]) (void)hipEventDestroy(c->ev_fill[g]);
+  delete c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_resize(moe_cache c, int32_t new_capacity, void* new_arena, void* stream) {
+  if (!c) return MOE_E_INVALID;
+  if (c->state != State::Idle) return MOE_E_BUSY;
+  const int floor_c = c->d.umax;
+  if (new_capacity < floor_c || new_capacity > c->max_capacity) return MOE_E_CAPACITY;
+  if (new_arena && !aligned16(new_arena)) return MOE_E_INVALID;
+  if (!new_arena && new_capacity > c->arena_slots) return MOE_E_CAPACITY;
+  hipError_t e = launch_resize(c->v, new_capacity, c->max_capacity, c->d.E, c->arena, new_arena,
+                               c->d.S, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(c, e);
+  c->capacity = new_capacity;
+  if (new_arena) {
+    c->arena = new_arena;
+    c->arena_slots = new_capacity;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t T,
+                              const void* w_router, int32_t* topk_idx, float* topk_w,
+                              void* stream) {
+  if (!c) return MOE_E_INVALID;
+  if (c->state != State::Idle) return MOE_E_INVALID;
+  if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
+  if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_E_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
+  if (e == hipSuccess) e = hipEventRecord(c->ev_plan, s);
+  if (e != hipSuccess) return hip_fail(c, e);
+  c->state = State::Planned;
+  c->plan_T = T;
+  c->plan_layer = layer;
+  return MOE_OK;
+}
+
+moe_status moe_fill_misses(moe_cache c, int32_t groups, void* fill_stream) {
+  if (!c) return MOE_E_INVALID;
+  if (c->state != State::Planned) return MOE_E_INVALID;
+  if (groups < 1 || groups > kMaxGroups) return MOE_E_INVALID;
+  hipStream_t s = (hipStream_t)fill_stream;
+  // The plan is ready, and (same compute stream) the previous step's FFN has finished reading
+  // the victim slots.
+  hipError_t e = hipStreamWaitEvent(s, c->ev_plan, 0);
+  for (int g = 0; g < groups && e == hipSuccess; ++g) {
+    e = launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s);
+    if (e == hipSuccess) e = hipEventRecord(c->ev_fill[g], s);
+  }
+  if (e != hipSuccess) return hip_fail(c, e);
+  c->fill_groups = groups;
+  c->state = State::Filled;
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
+                          const void* shared_blob, void* y, void* stream) {
+  if (!c) return MOE_E_INVALID;
+  if (c->state != State::Filled) return MOE_E_INVALID;
+  if (layer != c->plan_layer || T != c->plan_T) return MOE_E_INVALID;
+  if (T > 0 && (!x || !y || !aligned16(x) || ((uintptr_t)y & 3))) return MOE_E_INVALID;
+  if (c->d.has_shared && T > 0 && (!shared_blob || !aligned16(shared_blob))) return MOE_E_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
+  const int G = c->fill_groups;
+  hipError_t e = hipSuccess;
+  if (T > 0) {
+    e = launch_ffn_decode(c->d, c->v, x, c->arena, nullptr, 0, 0, 1, T, nu, s);
+    if (e == hipSuccess && c->d.has_shared)
+      e = launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, 2, 0, 1, T, 1, s);
+  }
+  for (int g = 0; g < G && e == hipSuccess; ++g) {
+    e = hipStreamWaitEvent(s, c->ev_fill[g], 0);
+    if (e == hipSuccess && T > 0)
+      e = launch_ffn_decode(c->d, c->v, x, c->arena, nullptr, 1, g, G, T, (nu + G - 1) / G, s);
+  }
+  if (e == hipSuccess && T > 0) e = launch_combine(c->d, c->v, y, T, c->d.has_shared, s);
+  if (e != hipSuccess) return hip_fail(c, e);
+  c->state = State::Idle;
+  return MOE_OK;
+}
+
+moe_status moe_layer_step(moe_cache c, int32_t layer, const void* x, int32_t T,
+                          const void* w_router, const void* shared_blob, int32_t* topk_idx,
+                          float* topk_w, void* y, int32_t groups, void* compute_stream,
+                          void* fill_stream) {
+  if (!c) return MOE_E_INVALID;
+  if (groups <= 0) groups = 2;
+  if (groups > kMaxGroups) return MOE_E_INVALID;
+  if (c->state != State::Idle) return MOE_E_INVALID;
+  if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
+  if (T > 0 && (!x || !y || !w_router)) return MOE_E_INVALID;
+  if (c->d.has_shared && T > 0 && !shared_blob) return MOE_E_INVALID;
+  moe_status st = moe_route_classify(c, layer, x, T, w_router, topk_idx, topk_w, compute_stream);
+  if (st != MOE_OK) return st;
+  st = moe_fill_misses(c, groups, fill_stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_ffn(c, layer, x, T, shared_blob, y, compute_stream);
+}
+
+moe_status moe_cache_snapshot(moe_cache c, int32_t* key_of, int32_t* stamp, int32_t* slot_of,
+                              int32_t* n_occupied, int64_t* step, int32_t* capacity) {
+  if (!c) return MOE_E_INVALID;
+  if (c->state != State::Idle) return MOE_E_BUSY;
+  hipError_t e = hipDeviceSynchronize();
+  const size_t cap = (size_t)c->capacity;
+  if (e == hipSuccess && key_of) e = hipMemcpy(key_of, c->v.key_of, 4 * cap, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && stamp) e = hipMemcpy(stamp, c->v.stamp, 4 * cap, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && slot_of)
+    e = hipMemcpy(slot_of, c->v.slot_of, 4 * (size_t)c->d.L * c->d.E, hipMemcpyDeviceToHost);
+  int ctrl[CTRL_WORDS];
+  if (e == hipSuccess) e = hipMemcpy(ctrl, c->v.ctrl, sizeof(ctrl), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  if (n_occupied) *n_occupied = ctrl[CTRL_N];
+  if (step) *step = (int64_t)(uint32_t)ctrl[CTRL_STEP_LO] | ((int64_t)ctrl[CTRL_STEP_HI] << 32);
+  if (capacity) *capacity = ctrl[CTRL_C];
+  if (ctrl[CTRL_ERR] & ERR_CAPACITY) return MOE_E_CAPACITY;
+  return MOE_OK;
+}
+
+moe_status moe_plan_read(moe_cache c, moe_plan_host* o) {
+  if (!c || !o) return MOE_E_INVALID;
+  hipError_t e = hipDeviceSynchronize();
+  int hdr[HDR_WORDS];
+  if (e == hipSuccess) e = hipMemcpy(hdr, c->v.hdr, sizeof(hdr), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  const int nu = hdr[HDR_NU], nm = hdr[HDR_NMISS], T = hdr[HDR_T];
+  o->n_unique = nu;
+  o->n_hit = hdr[HDR_NHIT];
+  o->n_miss = nm;
+  o->layer = hdr[HDR_LAYER];
+  o->step = (int64_t)(uint32_t)hdr[HDR_STEP_LO] | ((int64_t)hdr[HDR_STEP_HI] << 32);
+  std::vector<int> hit(nu > 0 ? nu : 1);
+  auto cp = [&](void* dst, const void* src, size_t n) {
+    if (e == hipSuccess && dst && n) e = hipMemcpy(dst, src, n, hipMemcpyDeviceToHost);
+  };
+  cp(o->unique, c->v.U, 4 * (size_t)nu);
+  cp(o->slot, c->v.u_slot, 4 * (size_t)nu);
+  cp(hit.data(), c->v.u_hit, 4 * (size_t)nu);
+  cp(o->miss_key, c->v.miss_key, 4 * (size_t)nm);
+  cp(o->miss_slot, c->v.miss_slot, 4 * (size_t)nm);
+  cp(o->miss_victim, c->v.miss_victim, 4 * (size_t)nm);
+  cp(o->count, c->v.count, 4 * (size_t)nu);
+  cp(o->perm, c->v.perm, 4 * (size_t)T * c->d.K);
+  if (e != hipSuccess) return hip_fail(c, e);
+  if (o->hit)
+    for (int i = 0; i < nu; ++i) o->hit[i] = (uint8_t)hit[i];
+  return MOE_OK;
+}
+
+moe_status moe_stats(moe_cache c, moe_counters* out) {
+  if (!c || !out) return MOE_E_INVALID;
+  unsigned long long s[STAT_WORDS];
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(s, c->v.stats, sizeof(s), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  out->steps = (int64_t)s[STAT_STEPS];
+  out->hits = (int64_t)s[STAT_HITS];
+  out->misses = (int64_t)s[STAT_MISSES];
+  out->bytes_filled = (int64_t)s[STAT_BYTES];
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_INVALID: return "invalid argument or call order";
+    case MOE_E_CAPACITY: return "capacity out of range";
+    case MOE_E_BUSY: return "a step is in flight";
+    case MOE_E_HIP: return "HIP runtime error";
+    case MOE_E_NOMEM: return "pinned host memory unavailable";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_last_hip_error(moe_cache c) { return c ? c->last_hip : 0; }
+
+}  // extern "C"

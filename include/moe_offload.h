@@ -1,0 +1,199 @@
+/* moe_offload.h - C ABI of the expert-offload MoE layer step on one MI355X (gfx950).
+ *
+ * One MoE layer step: router GEMM, renormalised softmax top-k, per-step dedup of
+ * the selected experts, hit/miss classification against one GPU slot cache shared
+ * by all MoE layers and keyed by (layer, expert), LRU victim selection and slot
+ * table update, miss fills from a pinned host expert pool into the cache slots on
+ * a side stream in double-buffered groups, and the SwiGLU expert FFN over the
+ * tokens gathered per expert; plus elastic resize of the cache at a safe point.
+ *
+ * Sources (the FreeToken pages):
+ *  - FreeToken paper summary (agihunt.info, arXiv 2608.16157), memory-architecture
+ *    paragraph: full expert pool in host memory, non-expert weights on the GPU, the
+ *    rest of VRAM one elastic expert cache shared by all MoE layers with slots
+ *    managed by the logical id (layer, expert).
+ *  - same page, execution-layer paragraph: per layer one kernel does routing dedup,
+ *    hit classification and LRU victim selection with no per-layer host sync; the
+ *    cache is rebuilt at a scheduler safe point when the VRAM budget changes;
+ *    weights are stored in their runtime layout so a load lands in its final place.
+ *  - same page, problem paragraph: VRAM budgets change during a session.
+ *  - same page, last paragraph: the host pool must be pinned and DMA-registered.
+ *  - "FreeToken vs vLLM on one RTX 3090" report, "FreeToken exploits MoE sparsity":
+ *    a fixed number of routed experts per token, an LRU expert cache, only selected
+ *    experts fetched on demand.
+ *  - "FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理", "FreeToken 解决的问题": while
+ *    one group of experts computes, the next group transfers (double buffering).
+ *
+ * Conventions.
+ *  - Every call returns moe_status.  Arguments are checked on the host before any
+ *    work is enqueued; a call that fails changes no state.  No exception crosses
+ *    the ABI.
+ *  - Device buffers, the pinned host pool and the streams belong to the caller.
+ *    The library owns only its opaque handle and the HIP events it creates; it
+ *    never allocates device memory (the caller passes a workspace of
+ *    moe_workspace_bytes()).  moe_host_pool_alloc() is a convenience wrapper
+ *    around hipHostMalloc for callers without their own pinned allocator.
+ *  - Streams are hipStream_t values passed as void*; NULL is the null stream.
+ *  - All step calls are asynchronous and stream ordered; none synchronises the
+ *    host and none allocates, so a caller may capture them into a hipGraph with
+ *    stream capture.  moe_cache_snapshot, moe_plan_read and moe_stats synchronise.
+ *  - Not thread-safe: one handle is driven from one host thread.
+ *
+ * Layouts (row-major).
+ *  - x: [T][hidden] bf16 layer input.  y: [T][hidden] bf16 layer output.
+ *  - w_router: [experts][hidden] bf16 router weights of the layer.
+ *  - topk_idx: [T][top_k] int32, by descending router logit, ties to the lower id.
+ *    topk_w: [T][top_k] fp32, renormalised softmax over the selected logits.
+ *  - host pool: layers*experts blobs of blob_bytes, blob (l, e) at offset
+ *    (l*experts + e)*blob_bytes.  A cache slot holds one blob, byte-identical.
+ *  - blob, bf16 (wfmt 0): Wgu[I][2][H] (gate row i then up row i), WdT[I][H].
+ *    fp8 (wfmt 1): e4m3fn codes Wgu[I][2][H], WdT[I][H], then fp32 scales
+ *    s_gu[I][2][H/128], s_d[I/128][H]; one scale per 128 contraction elements.
+ *    mxfp4 (wfmt 2): e2m1 codes two per byte (even element low nibble)
+ *    Wgu[I][2][H/2], WdT[I][H/2], then e8m0 scales s_gu[I][2][H/32], s_d[I/32][H].
+ *    H = hidden, I = inter.  WdT row i is column i of the down projection Wd[H][I].
+ *  - shared expert (has_shared): one more blob in the same format, resident on the
+ *    GPU, added to every token with weight 1; it is not cached and not pooled.
+ */
+#ifndef MOE_OFFLOAD_H
+#define MOE_OFFLOAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_E_INVALID (-1)  /* bad shape, pointer, format, size or call order */
+#define MOE_E_CAPACITY (-2) /* capacity below min(max_tokens*top_k, experts) or above max */
+#define MOE_E_BUSY (-3)     /* resize or snapshot while a step is in flight */
+#define MOE_E_HIP (-4)      /* a HIP runtime call failed; see moe_last_hip_error */
+#define MOE_E_NOMEM (-5)    /* pinned host allocation failed */
+
+#define MOE_FMT_BF16 0
+#define MOE_FMT_FP8_E4M3_K128 1
+#define MOE_FMT_MXFP4_K32 2
+
+typedef struct moe_cache_s* moe_cache;
+
+typedef struct {
+  int32_t layers;     /* MoE layers sharing the cache */
+  int32_t experts;    /* routed experts per layer, <= 1024 */
+  int32_t top_k;      /* experts selected per token, 1..16 */
+  int32_t hidden;     /* H, multiple of 256 */
+  int32_t inter;      /* I, SwiGLU intermediate size, multiple of 128 */
+  int32_t wfmt;       /* MOE_FMT_* */
+  int32_t has_shared; /* 1: one GPU-resident shared expert per layer */
+  int32_t max_tokens; /* largest T passed to any step call, 1..8 */
+  int64_t blob_bytes; /* must equal moe_blob_bytes(wfmt, hidden, inter) */
+} moe_shape;
+
+/* Plan of the last routed step, copied to the host (parity and tests). */
+typedef struct {
+  int32_t n_unique, n_hit, n_miss, layer;
+  int64_t step;
+  int32_t* unique;    /* [n_unique] distinct experts, ascending */
+  int32_t* slot;      /* [n_unique] cache slot of each, after the step */
+  uint8_t* hit;       /* [n_unique] 1 = was cached before the step */
+  int32_t* miss_key;  /* [n_miss] key = layer*experts + expert, ascending expert */
+  int32_t* miss_slot; /* [n_miss] slot filled */
+  int32_t* miss_victim; /* [n_miss] evicted key, or -1 for a free slot */
+  int32_t* count;     /* [n_unique] assignments per distinct expert */
+  int32_t* perm;      /* [T*top_k] assignment ids t*top_k+j grouped by expert, ascending t */
+} moe_plan_host;      /* caller-owned arrays sized for min(max_tokens*top_k, experts) / T*top_k */
+
+typedef struct {
+  int64_t steps, hits, misses, bytes_filled;
+} moe_counters;
+
+/* Bytes of one expert blob, or -1 for an unsupported shape. */
+int64_t moe_blob_bytes(int32_t wfmt, int32_t hidden, int32_t inter);
+
+/* Device workspace bytes for a cache of up to max_capacity slots. */
+size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_capacity);
+
+/* Pinned, device-accessible host memory for the expert pool (hipHostMalloc).
+ * Returns MOE_E_NOMEM when the allocation fails.  Free with moe_host_pool_free. */
+moe_status moe_host_pool_alloc(size_t bytes, void** out);
+moe_status moe_host_pool_free(void* p);
+
+/* Create a cache of `capacity` slots (slot i at slot_arena + i*blob_bytes) over the
+ * pinned host pool.  slot_arena must hold max_capacity slots; workspace must be
+ * moe_workspace_bytes(shape, max_capacity) bytes of device memory, 256-byte
+ * aligned.  host_pool must come from hipHostMalloc (moe_host_pool_alloc).  The
+ * cache starts empty; its state is initialised on `stream` (asynchronously).
+ * Errors: MOE_E_INVALID, MOE_E_CAPACITY (capacity < min(max_tokens*top_k, experts)
+ * or capacity > max_capacity), MOE_E_NOMEM (pool not device-accessible), MOE_E_HIP. */
+moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t max_capacity,
+                            void* slot_arena, void* workspace, const void* host_pool,
+                            void* stream, moe_cache* out);
+
+moe_status moe_cache_destroy(moe_cache cache);
+
+/* Elastic resize at a safe point (no step in flight: the last routed step has had
+ * its FFN issued).  Keeps the new_capacity most recently used experts; survivors in
+ * slots >= new_capacity move into the holes below it, in ascending slot order; stamps
+ * are kept.  Growing adds empty slots.  new_arena: NULL keeps the current arena
+ * (slots >= new_capacity become unused; growing in place is limited to the slots the
+ * current arena holds); otherwise a device buffer of new_capacity slots that receives
+ * every surviving slot and becomes the arena, after which the old arena may be
+ * released once `stream` has passed this call.  Stream ordered.
+ * MOE_E_BUSY if a step is in flight, MOE_E_CAPACITY outside
+ * [min(max_tokens*top_k, experts), max_capacity]. */
+moe_status moe_cache_resize(moe_cache cache, int32_t new_capacity, void* new_arena, void* stream);
+
+/* Router GEMM + top-k + dedup + classification + LRU victims + slot-table update
+ * for `layer`, in one kernel on `stream`.  x: [T][hidden] bf16; w_router:
+ * [experts][hidden] bf16.  topk_idx/topk_w may be NULL.  Writes the step plan into
+ * the workspace; the next moe_fill_misses and moe_expert_ffn use it.
+ * MOE_E_INVALID if T > max_tokens, layer out of range, or the previous plan has
+ * not had its FFN issued. */
+moe_status moe_route_classify(moe_cache cache, int32_t layer, const void* x, int32_t T,
+                              const void* w_router, int32_t* topk_idx, float* topk_w,
+                              void* stream);
+
+/* Copy the missed blobs of the last plan from the host pool into their slots on
+ * `fill_stream`, in `groups` double-buffered groups (groups >= 1; group g holds the
+ * misses [g*m/groups, (g+1)*m/groups) of the m misses, ascending expert).  Waits for
+ * the plan and for the previous step's FFN (a victim slot may still be read). */
+moe_status moe_fill_misses(moe_cache cache, int32_t groups, void* fill_stream);
+
+/* SwiGLU expert FFN and combine for the last plan on `stream`: hit experts first,
+ * then each fill group once its copy has landed.  y: [T][hidden] bf16.
+ * shared_blob: the layer's shared-expert blob on the GPU, or NULL when
+ * has_shared == 0.  MOE_E_INVALID if the fills of the plan were not issued. */
+moe_status moe_expert_ffn(moe_cache cache, int32_t layer, const void* x, int32_t T,
+                          const void* shared_blob, void* y, void* stream);
+
+/* One whole layer step: moe_route_classify + moe_fill_misses(groups) +
+ * moe_expert_ffn.  groups <= 0 picks 2. */
+moe_status moe_layer_step(moe_cache cache, int32_t layer, const void* x, int32_t T,
+                          const void* w_router, const void* shared_blob, int32_t* topk_idx,
+                          float* topk_w, void* y, int32_t groups, void* compute_stream,
+                          void* fill_stream);
+
+/* Synchronous copies of the cache state: key_of[capacity], stamp[capacity] (step
+ * of last use, -1 empty), slot_of[layers*experts] (-1 absent), occupancy n and the
+ * step counter.  Any pointer may be NULL. */
+moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int32_t* stamp,
+                              int32_t* slot_of, int32_t* n_occupied, int64_t* step,
+                              int32_t* capacity);
+
+/* Synchronous copy of the last plan (see moe_plan_host). */
+moe_status moe_plan_read(moe_cache cache, moe_plan_host* out);
+
+/* Synchronous read of the device-side counters. */
+moe_status moe_stats(moe_cache cache, moe_counters* out);
+
+const char* moe_status_string(moe_status s);
+
+/* The hipError_t of the last MOE_E_HIP returned on this handle (0 if none). */
+int32_t moe_last_hip_error(moe_cache cache);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_OFFLOAD_H */

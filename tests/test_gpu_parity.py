@@ -1,0 +1,174 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle, step by step.
+
+Integer results (expert indices, distinct experts, hit flags, miss slots, victims, per-expert
+token lists, key_of / stamp / slot_of / occupancy) must match bit-exactly; routing weights within
+1e-6 relative; layer outputs within relative L2 2e-2 (bf16) or 5e-2 (fp8, MXFP4)."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from parity import compare_step, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _bench(wl, **kw):
+    from expert_cache_offload_amd.runner import Workbench
+    return Workbench(wl, **kw)
+
+
+def _oracle(wb):
+    from oracle.step import Oracle
+    shared = (lambda l: wb.shared_np[l]) if wb.wl.has_shared else None
+    return Oracle(wb.wl, wb.pool, wb.router_np, shared)
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_parity(wb, n_tok, ffn_every=1, state_every=1, slot_bytes=False, parts=False):
+    wl = wb.wl
+    orc = _oracle(wb)
+    errs = []
+    for t in range(n_tok):
+        if wl.resize_at >= 0 and t == wl.resize_at:
+            moves = orc.resize(wl.resize_capacity)
+            wb.resize(wl.resize_capacity)
+            key_of, stamp, slot_of, n, step, cap = wb.snapshot()
+            assert cap == wl.resize_capacity and n == orc.cache.n
+            assert list(key_of) == orc.cache.key_of and list(stamp) == orc.cache.stamp
+            for src, dst in moves:  # moved blobs arrived intact
+                k = orc.cache.key_of[dst]
+                assert np.array_equal(wb.slot_bytes(dst), orc.blob(k))
+        for l in range(wl.layers):
+            (wb.step_parts if parts else wb.step)(t, l)
+            with_ffn = (t * wl.layers + l) % ffn_every == 0
+            x = wb.acts_np[t, l] if wl.kind == "decode" else wb.acts_np[l]
+            ref = orc.layer_step(t, l, x, with_ffn)
+            err = compare_step(wb, ref, f"{wl.name} t={t} l={l}",
+                               check_state=(t * wl.layers + l) % state_every == 0)
+            if err is not None:
+                errs.append(err)
+            if slot_bytes:
+                for sl, k in enumerate(ref.rec.key_of):
+                    if k >= 0:
+                        assert np.array_equal(wb.slot_bytes(sl), orc.blob(k)), (t, l, sl, k)
+    return errs
+
+
+def test_tiny_decode_every_step_and_slot_bytes():
+    wl = mi.WORKLOADS["tiny"]
+    _log(f"case {wl.name}")
+    with _bench(wl) as wb:
+        errs = run_parity(wb, wl.token_steps, slot_bytes=True)
+        st = wb.stats()
+    assert st["steps"] == wl.token_steps
+    assert st["hits"] + st["misses"] > 0 and st["bytes_filled"] == st["misses"] * wl.blob_bytes
+    _log(f"tiny: max rel-L2 {max(errs):.2e}, misses {st['misses']}")
+
+
+def test_tiny_through_separate_calls():
+    wl = mi.WORKLOADS["tiny"].with_steps(24)
+    with _bench(wl, groups=3) as wb:
+        run_parity(wb, 24, parts=True)
+
+
+@pytest.mark.parametrize("groups", [1, 2, 8])
+def test_bf16_decode_multilayer_evictions(groups):
+    """35B-A3B expert shape (H 2048, 128 experts top-8, I 768) with 4 layers sharing a 30% cache."""
+    wl = mi.WORKLOADS["qwen35b_decode"].with_layers(4).with_steps(24)
+    _log(f"case {wl.name} groups={groups} C={wl.capacity}")
+    with _bench(wl, groups=groups) as wb:
+        errs = run_parity(wb, wl.token_steps, ffn_every=7)
+    _log(f"bf16 4-layer: max rel-L2 {max(errs):.2e}")
+
+
+def test_fp8_decode_with_shared_expert():
+    """284B-like shape: H 4096, 256 experts top-8 + shared expert, fp8 e4m3 1x128 blocks."""
+    wl = mi.WORKLOADS["dsv4_fp8_decode"].with_layers(2).with_steps(12)
+    _log(f"case {wl.name} C={wl.capacity}")
+    with _bench(wl) as wb:
+        errs = run_parity(wb, wl.token_steps, ffn_every=5)
+    _log(f"fp8: max rel-L2 {max(errs):.2e}")
+
+
+def test_mxfp4_four_streams_with_resize():
+    """753B-like shape: H 6144, 256 experts top-8, MXFP4, 4 streams per step with cross-request
+    dedup; the cache shrinks from 40% to 15% of the pool at a safe point."""
+    wl = dataclasses.replace(mi.WORKLOADS["glm_mxfp4_4stream"].with_layers(2), token_steps=16,
+                             resize_at=8)
+    _log(f"case {wl.name} C={wl.capacity}->{wl.resize_capacity}")
+    with _bench(wl) as wb:
+        errs = run_parity(wb, wl.token_steps, ffn_every=6)
+    _log(f"mxfp4: max rel-L2 {max(errs):.2e}")
+
+
+def test_capacity_at_floor_and_everything_fits():
+    base = mi.WORKLOADS["qwen35b_decode"].with_layers(2).with_steps(10)
+    for cap in (8, 2 * 128):  # C = top_k (every step evicts), C = all keys (only cold misses)
+        wl = dataclasses.replace(base, fixed_capacity=cap)
+        _log(f"case capacity {cap}")
+        with _bench(wl) as wb:
+            run_parity(wb, wl.token_steps, ffn_every=9)
+            st = wb.stats()
+        if cap == 256:
+            assert st["misses"] <= 256
+
+
+def test_empty_step_advances_counter_only():
+    wl = mi.WORKLOADS["tiny"].with_steps(4)
+    with _bench(wl) as wb:
+        wb.step(0, 0)
+        before = wb.snapshot()
+        wb.step(1, 0, T=0)
+        p = wb.plan()
+        after = wb.snapshot()
+        assert p["n_unique"] == 0 and p["n_miss"] == 0
+        assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+        assert after[4] == before[4] + 1
+
+
+def test_resize_into_new_arena_keeps_contents():
+    import torch
+    wl = mi.WORKLOADS["tiny"].with_steps(20)
+    with _bench(wl, capacity=8, max_capacity=12) as wb:
+        orc = _oracle(wb)
+        for t in range(10):
+            wb.step(t, 0)
+            orc.layer_step(t, 0, wb.acts_np[t, 0], False)
+        new = torch.empty(5 * wl.blob_bytes, dtype=torch.uint8, device=wb.dev)
+        wb.sync()
+        wb.resize(5, new)
+        orc.resize(5)
+        key_of, stamp, slot_of, n, step, cap = wb.snapshot()
+        assert list(key_of) == orc.cache.key_of and n == orc.cache.n == 5
+        for sl, k in enumerate(orc.cache.key_of):
+            assert np.array_equal(wb.slot_bytes(sl), orc.blob(k))
+        with pytest.raises(Exception):
+            wb.resize(12)  # the 5-slot arena cannot grow in place
+        bigger = torch.empty(12 * wl.blob_bytes, dtype=torch.uint8, device=wb.dev)
+        wb.resize(12, bigger)
+        orc.resize(12)
+        for t in range(10, 20):
+            wb.step(t, 0)
+            ref = orc.layer_step(t, 0, wb.acts_np[t, 0], True)
+            compare_step(wb, ref, f"after growth t={t}")
+        for sl, k in enumerate(orc.cache.key_of):
+            if k >= 0:
+                assert np.array_equal(wb.slot_bytes(sl), orc.blob(k))
+
+
+def test_full_size_bf16_decode_sampled():
+    """The 48-layer 35B-A3B shape at full size (58 GB pinned pool, 1,843 slots): every integer
+    result for the first 96 token steps (4,608 layer steps), outputs sampled."""
+    wl = mi.WORKLOADS["qwen35b_decode"].with_steps(96)
+    _log(f"case {wl.name} full size, 96 tokens")
+    with _bench(wl) as wb:
+        errs = run_parity(wb, wl.token_steps, ffn_every=97, state_every=53)
+        st = wb.stats()
+    _log(f"full-size: max rel-L2 {max(errs):.2e}; miss rate {st['misses'] / (st['hits'] + st['misses']):.3f}")
