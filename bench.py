@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""MoE-layer decode throughput of the expert-offload stack on one MI355X.
+
+Workload (default): the 48-layer 35B-A3B-shaped MoE stack - hidden 2048, 128 experts top-8
+with renormalised softmax, SwiGLU intermediate 768, bf16 expert weights N(0, 0.02) in a
+pinned host pool (58 GB), one LRU slot cache shared by all layers holding 30% of the pool
+(1,843 slots), AR(1) activations per layer, batch 1, seed 0, cold cache.  One step = one
+decode token through all 48 layer steps (route, dedup, classify, LRU, fills, FFN).  The
+first --warmup tokens are untimed; exactly --steps tokens are timed.
+
+Reported (one JSON line): decode tokens/s of the stack; the FFN weight-streaming kernel
+against the MI355X HBM roofline (achieved = expert-weight bytes the FFN kernels were given
+/ their event-measured duration); fill bandwidth against pinned hipMemcpyAsync H2D measured
+on the same box; the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def _die_multi_gpu(n: int) -> None:
+    print(f"bench.py: this build runs on one GPU only (--gpus {n} requested); "
+          "the expert-offload path is measured on a single MI355X.", file=sys.stderr)
+    sys.exit(2)
+
+
+def h2d_memcpy_probe(pool_addr: int, pool_bytes: int, blob: int, dev_buf_ptr: int,
+                     dev_buf_bytes: int) -> dict:
+    """Pinned host -> device hipMemcpyAsync bandwidth, back-to-back blob-sized copies and one
+    large copy, from the same pinned pool the fills read."""
+    hip = ctypes.CDLL("libamdhip64.so.7")  # by soname: the runtime already loaded by PyTorch
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    hip.hipStreamSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipStreamCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    s = ctypes.c_void_p()
+    assert hip.hipStreamCreate(ctypes.byref(s)) == 0
+    H2D = 1
+    out = {}
+    n = min(64, dev_buf_bytes // blob, pool_bytes // blob)
+
+    def run(size, count):
+        # warm once, then time
+        assert hip.hipMemcpyAsync(dev_buf_ptr, pool_addr, size, H2D, s) == 0
+        hip.hipStreamSynchronize(s)
+        t0 = time.perf_counter()
+        for i in range(count):
+            src = pool_addr + ((i * 7919) % (pool_bytes // size)) * size
+            dst = dev_buf_ptr + (i % (dev_buf_bytes // size)) * size
+            assert hip.hipMemcpyAsync(dst, src, size, H2D, s) == 0
+        hip.hipStreamSynchronize(s)
+        return size * count / (time.perf_counter() - t0) / 1e9
+
+    out["blob_GBps"] = run(blob, n)
+    big = min(1 << 30, dev_buf_bytes, pool_bytes)
+    out["large_GBps"] = run(big, 4)
+    out["large_bytes"] = big
+    hip.hipStreamDestroy(s)
+    return out
+
+
+def cpu_baseline(wb, tokens: int) -> dict:
+    """The float64 oracle as it stands, on the first `tokens` token steps of the workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle.step import Oracle
+    wl = wb.wl
+    shared = (lambda l: wb.shared_np[l]) if wl.has_shared else None
+    orc = Oracle(wl, wb.pool, wb.router_np, shared)
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        for l in range(wl.layers):
+            x = wb.acts_np[t, l] if wl.kind == "decode" else wb.acts_np[l]
+            orc.layer_step(t, l, x, True)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": tokens * wl.tokens_per_step / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {tokens} token step(s) x {wl.layers} layers of the same workload, "
+                      f"full float64 route+top-k+dedup+LRU+SwiGLU FFN, {dt:.1f} s",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def _ffn_source_hash() -> str:
+    here = os.path.dirname(os.path.abspath(__file__))
+    p = os.path.join(here, "expert_cache_offload_amd", "csrc", "ffn_decode.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(name: str) -> float | None:
+    """HBM bytes per FFN launch from a committed counter summary, if it was taken on the
+    current kernel source (its header line records the source hash)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    p = os.path.join(here, "profiles", name)
+    if not os.path.exists(p):
+        return None
+    h = _ffn_source_hash()
+    val = None
+    src_ok = False
+    for line in open(p):
+        if line.startswith("ffn_source_sha256_16:") and line.split(":", 1)[1].strip() == h:
+            src_ok = True
+        if line.startswith("hbm_bytes_per_ffn_launch:"):
+            val = float(line.split(":", 1)[1])
+    return val if src_ok else None
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480, help="timed decode tokens")
+    ap.add_argument("--warmup", type=int, default=32, help="untimed decode tokens before")
+    ap.add_argument("--workload", default="qwen35b_decode")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (0 = workload's)")
+    ap.add_argument("--groups", type=int, default=2, help="fill groups per step")
+    ap.add_argument("--cpu-tokens", type=int, default=1, help="oracle sample (token steps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="no per-kernel events")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        _die_multi_gpu(max(args.gpus, world))
+
+    import torch
+
+    import moe_inputs as mi
+    from expert_cache_offload_amd import moe_profile_enable, moe_profile_read
+    from expert_cache_offload_amd.runner import Workbench
+
+    wl = mi.WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_layers(args.layers)
+    n_tok = args.warmup + args.steps
+    if wl.kind != "decode":
+        raise SystemExit("bench.py times decode workloads")
+    wl = wl.with_steps(max(n_tok, args.cpu_tokens))
+    print(f"[bench] workload {wl.name}: L={wl.layers} H={wl.hidden} E={wl.experts} k={wl.top_k} "
+          f"I={wl.inter} fmt={wl.fmt} C={wl.capacity} pool={wl.pool_bytes / 1e9:.2f} GB",
+          file=sys.stderr, flush=True)
+    t_setup = time.perf_counter()
+    wb = Workbench(wl, groups=args.groups)
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+    L = wl.layers
+    for t in range(args.warmup):
+        for l in range(L):
+            wb.step(t, l)
+    wb.sync()
+    st0 = wb.stats()
+    if not args.no_profile:
+        moe_profile_enable(wb.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, n_tok):
+        for l in range(L):
+            wb.step(t, l)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    prof = moe_profile_read(wb.handle) if not args.no_profile else None
+    st1 = wb.stats()
+    hits = st1["hits"] - st0["hits"]
+    misses = st1["misses"] - st0["misses"]
+    fill_bytes = st1["bytes_filled"] - st0["bytes_filled"]
+    tokens = args.steps * wl.tokens_per_step
+    tok_s = tokens / wall
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s -> {tok_s:.2f} tok/s; "
+          f"miss rate {misses / max(1, hits + misses):.3f}", file=sys.stderr, flush=True)
+
+    # pinned hipMemcpyAsync H2D on this machine (denominator of the fill bar)
+    scratch = torch.empty(min(1 << 30, wl.capacity * wl.blob_bytes), dtype=torch.uint8,
+                          device=wb.dev)
+    h2d = h2d_memcpy_probe(wb.pool_addr, wb.pool_bytes, wl.blob_bytes, scratch.data_ptr(),
+                           scratch.numel())
+    del scratch
+
+    roofline = None
+    fill = {"bytes": fill_bytes, "link_GBps": fill_bytes / wall / 1e9,
+            "h2d_memcpy_blob_GBps": h2d["blob_GBps"], "h2d_memcpy_1GiB_GBps": h2d["large_GBps"]}
+    if prof is not None:
+        ffn_bytes = prof["ffn_weight_bytes"]
+        ffn_s = prof["ffn_ms"] / 1e3
+        achieved = ffn_bytes / ffn_s / 1e9 if ffn_s > 0 else 0.0
+        traffic = _traffic_from_profile(f"ffn_decode_{wl.name}_pmc.txt")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "kernel": "ffn_kernel",
+                    "launches": prof["ffn_launches"],
+                    "avg_launch_us": round(prof["ffn_ms"] * 1e3 / max(1, prof["ffn_launches"]), 2),
+                    "algorithmic_bytes_per_launch": ffn_bytes / max(1, prof["ffn_launches"])}
+        fill_kernel_gbps = prof["fill_bytes"] / (prof["fill_ms"] / 1e3) / 1e9 if prof["fill_ms"] else 0
+        fill.update({"kernel_GBps": round(fill_kernel_gbps, 2),
+                     "kernel_frac_of_memcpy": round(fill_kernel_gbps / h2d["blob_GBps"], 3),
+                     "fill_launches": prof["fill_launches"],
+                     "link_busy_frac": round(prof["fill_ms"] / 1e3 / wall, 3)})
+        extra = {"route_us": round(prof["route_ms"] * 1e3 / max(1, prof["route_launches"]), 2)}
+    else:
+        extra = {}
+    fill["link_frac_of_memcpy"] = round(fill["link_GBps"] / h2d["blob_GBps"], 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wb, args.cpu_tokens)
+        print(f"[bench] oracle {cpu['value']:.4f} tok/s ({cpu['seconds']:.1f} s)", file=sys.stderr,
+              flush=True)
+    wb.close()
+
+    dtype = {0: "bf16", 1: "fp8", 2: "mxfp4"}[wl.fmt]
+    line = {
+        "metric": "MoE decode tokens/s per layer stack + HBM GB/s fraction; miss-fill PCIe GB/s",
+        "value": round(tok_s, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "hidden": wl.hidden,
+                   "experts": wl.experts, "top_k": wl.top_k, "inter": wl.inter,
+                   "cache_slots": wl.capacity, "pool_bytes": wl.pool_bytes,
+                   "tokens_per_step": wl.tokens_per_step, "fill_groups": args.groups,
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "fill": fill,
+        "miss_rate": round(misses / max(1, hits + misses), 4),
+        "misses_per_token": round(misses / max(1, tokens), 2),
+        **extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,10 +12,17 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_offload.so")
+# MOE_OFFLOAD_LIB selects another build of the same ABI (e.g. an instrumented one).
+LIB_PATH = os.environ.get("MOE_OFFLOAD_LIB") or os.path.join(_HERE, "libmoe_offload.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_CAPACITY, MOE_E_BUSY, MOE_E_HIP, MOE_E_NOMEM = 0, -1, -2, -3, -4, -5
 MOE_FMT_BF16, MOE_FMT_FP8_E4M3_K128, MOE_FMT_MXFP4_K32 = 0, 1, 2
+
+# PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7).  Loading torch
+# first makes the library's HIP dependency resolve to that already-loaded runtime, so device
+# memory and streams created by PyTorch and the library's launches share one runtime; loading
+# the library first would bring up a second runtime and PyTorch would then find no GPU.
+import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -48,6 +55,13 @@ class MoeCounters(ctypes.Structure):
                 ("misses", ctypes.c_int64), ("bytes_filled", ctypes.c_int64)]
 
 
+class MoeProfile(ctypes.Structure):
+    _fields_ = [("route_launches", ctypes.c_int64), ("fill_launches", ctypes.c_int64),
+                ("ffn_launches", ctypes.c_int64), ("route_ms", ctypes.c_double),
+                ("fill_ms", ctypes.c_double), ("ffn_ms", ctypes.c_double),
+                ("fill_bytes", ctypes.c_int64), ("ffn_weight_bytes", ctypes.c_int64)]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "moe_blob_bytes": (_i64, [_i32, _i32, _i32]),
@@ -65,6 +79,8 @@ _SIGS = {
     "moe_cache_snapshot": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_plan_read": (_i32, [_vp, ctypes.POINTER(MoePlanHost)]),
     "moe_stats": (_i32, [_vp, ctypes.POINTER(MoeCounters)]),
+    "moe_profile_enable": (_i32, [_vp, _i32]),
+    "moe_profile_read": (_i32, [_vp, ctypes.POINTER(MoeProfile)]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_last_hip_error": (_i32, [_vp]),
 }
@@ -201,6 +217,16 @@ def moe_stats(handle: int) -> dict:
     return {"steps": c.steps, "hits": c.hits, "misses": c.misses, "bytes_filled": c.bytes_filled}
 
 
+def moe_profile_enable(handle: int, enable: bool = True) -> None:
+    _check(_lib.moe_profile_enable(handle, int(enable)), "moe_profile_enable", handle)
+
+
+def moe_profile_read(handle: int) -> dict:
+    p = MoeProfile()
+    _check(_lib.moe_profile_read(handle, ctypes.byref(p)), "moe_profile_read", handle)
+    return {f: getattr(p, f) for f, _ in MoeProfile._fields_}
+
+
 def moe_status_string(status: int) -> str:
     return _lib.moe_status_string(status).decode()
 
@@ -209,5 +235,5 @@ def moe_last_hip_error(handle: int) -> int:
     return int(_lib.moe_last_hip_error(handle))
 
 
-__all__ = [n for n in _SIGS] + ["MoeShape", "MoePlanHost", "MoeCounters", "MoeError",
+__all__ = [n for n in _SIGS] + ["MoeShape", "MoePlanHost", "MoeCounters", "MoeProfile", "MoeError",
                                 "make_shape", "LIB_PATH"]

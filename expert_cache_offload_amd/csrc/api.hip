@@ -15,12 +15,10 @@ hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const v
                              int* out_idx, float* out_w, int layer, int T, hipStream_t s);
 size_t route_plan_lds_bytes(const Dims& d);
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
-                             const void* shared_blob, int mode, int group, int ngroups, int T,
-                             int max_entries, hipStream_t s);
-size_t ffn_decode_lds_bytes(const Dims& d, int ntok);
+                             const void* shared_blob, void* y, int sel, int group, int ngroups,
+                             int T, int max_entries, int with_combine, hipStream_t s);
 int decode_ntok(int T);
-hipError_t launch_combine(const Dims& d, const Dev& v, void* y, int T, int with_shared,
-                          hipStream_t s);
+int down_columns_per_block(int fmt);
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
                        int ngroups, int grid, hipStream_t s);
 hipError_t launch_init(const Dev& v, int max_capacity, int n_keys, int capacity, hipStream_t s);
@@ -33,26 +31,22 @@ using namespace moe;
 
 namespace {
 
-constexpr int kMaxGroups = 64;
+constexpr int kMaxGroups = kMaxFillGroups;
 constexpr int kMaxCapacity = 4096;  // LDS-resident LRU stamps and the resize sort
-constexpr int kFillGrid = 256;
+// Fill workgroups: 32 saturate the PCIe link (57 GB/s measured) while leaving HBM streaming
+// of concurrent kernels untouched; 256 workgroups collapse a concurrent HBM stream to <2%.
+constexpr int kFillGrid = 32;
 
 enum class State { Idle, Planned, Filled };
 
 struct Layout {
   size_t key_of, stamp, slot_of, ctrl, stats, hdr, U, u_slot, u_hit, hit_list, miss_list,
       miss_key, miss_slot, miss_victim, count, offset, perm, inv_pos, tk_idx, tk_w, logits,
-      partial, shared_partial, moves, total;
+      act, act_shared, yexp, yexp_shared, ent, row_tok, row_w, moves, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int rows_per_workgroup(int fmt, int inter) {
-  // R must divide the scale block of the down projection (128 for fp8, 32 for MXFP4).
-  int R = fmt == MOE_FMT_BF16 ? 16 : fmt == MOE_FMT_FP8_E4M3_K128 ? 64 : 32;
-  while (R > 1 && inter % R) R >>= 1;
-  return R;
-}
 
 Dims make_dims(const moe_shape& s, int max_capacity) {
   Dims d{};
@@ -67,8 +61,9 @@ Dims make_dims(const moe_shape& s, int max_capacity) {
   d.amax = s.max_tokens * s.top_k;
   d.umax = d.amax < s.experts ? d.amax : s.experts;
   d.max_capacity = max_capacity;
-  d.R = rows_per_workgroup(s.wfmt, s.inter);
-  d.nR = s.inter / d.R;
+  // Split the down projection's rows in two when one launch would not fill the chip.
+  const int col_blocks = s.hidden / down_columns_per_block(s.wfmt);
+  d.RS = (d.umax * col_blocks < 512) ? 2 : 1;
   d.S = s.blob_bytes;
   return d;
 }
@@ -103,9 +98,13 @@ Layout make_layout(const Dims& d) {
   L.tk_idx = take(I4 * d.amax);
   L.tk_w = take(sizeof(float) * d.amax);
   L.logits = take(sizeof(double) * (size_t)d.max_tokens * d.E);
-  L.partial = take(sizeof(float) * (size_t)d.amax * d.nR * d.H);
-  L.shared_partial =
-      take(d.has_shared ? sizeof(float) * (size_t)d.max_tokens * d.nR * d.H : 256);
+  L.act = take(sizeof(float) * (size_t)d.amax * d.I);
+  L.act_shared = take(d.has_shared ? sizeof(float) * (size_t)d.max_tokens * d.I : 256);
+  L.yexp = take(sizeof(float) * (size_t)d.amax * d.RS * d.H);
+  L.yexp_shared = take(d.has_shared ? sizeof(float) * (size_t)d.max_tokens * d.RS * d.H : 256);
+  L.ent = take(sizeof(int) * 4 * (size_t)d.umax);
+  L.row_tok = take(I4 * d.amax);
+  L.row_w = take(sizeof(float) * d.amax);
   L.moves = take(I4 * 2 * (size_t)d.max_capacity);
   L.total = o;
   return L;
@@ -135,8 +134,13 @@ Dev make_dev(void* ws, const Layout& L) {
   v.tk_idx = (int*)(b + L.tk_idx);
   v.tk_w = (float*)(b + L.tk_w);
   v.logits = (double*)(b + L.logits);
-  v.partial = (float*)(b + L.partial);
-  v.shared_partial = (float*)(b + L.shared_partial);
+  v.act = (float*)(b + L.act);
+  v.act_shared = (float*)(b + L.act_shared);
+  v.yexp = (float*)(b + L.yexp);
+  v.yexp_shared = (float*)(b + L.yexp_shared);
+  v.ent = (int4*)(b + L.ent);
+  v.row_tok = (int*)(b + L.row_tok);
+  v.row_w = (float*)(b + L.row_w);
   v.moves = (int*)(b + L.moves);
   return v;
 }
@@ -160,7 +164,81 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
+// Timing of the library's own launches with event pairs from a reusable ring.
+struct Profiler {
+  enum Kind { ROUTE = 0, FILL = 1, FFN = 2, NKIND = 3 };
+  static constexpr int kRing = 4096;
+  bool on = false;
+  std::vector<hipEvent_t> a, b;
+  std::vector<int> kind;
+  size_t head = 0, pending = 0;
+  double ms[NKIND] = {0, 0, 0};
+  int64_t launches[NKIND] = {0, 0, 0};
+  unsigned long long stats0[STAT_WORDS] = {};
+
+  hipError_t ensure() {
+    if (!a.empty()) return hipSuccess;
+    a.resize(kRing);
+    b.resize(kRing);
+    kind.resize(kRing);
+    for (int i = 0; i < kRing; ++i) {
+      hipError_t e = hipEventCreate(&a[i]);
+      if (e == hipSuccess) e = hipEventCreate(&b[i]);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  hipError_t harvest_one() {
+    const size_t i = (head + kRing - pending) % kRing;
+    hipError_t e = hipEventSynchronize(b[i]);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, a[i], b[i]);
+    if (e != hipSuccess) return e;
+    ms[kind[i]] += t;
+    launches[kind[i]] += 1;
+    --pending;
+    return hipSuccess;
+  }
+  hipError_t harvest_all() {
+    while (pending) {
+      hipError_t e = harvest_one();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  template <class F>
+  hipError_t timed(int k, hipStream_t s, F launch) {
+    if (!on) return launch();
+    if (pending == (size_t)kRing) {
+      hipError_t e = harvest_one();
+      if (e != hipSuccess) return e;
+    }
+    const size_t i = head;
+    hipError_t e = hipEventRecord(a[i], s);
+    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess) e = hipEventRecord(b[i], s);
+    if (e != hipSuccess) return e;
+    kind[i] = k;
+    head = (head + 1) % kRing;
+    ++pending;
+    return hipSuccess;
+  }
+  void reset() {
+    for (int k = 0; k < NKIND; ++k) {
+      ms[k] = 0;
+      launches[k] = 0;
+    }
+  }
+  void destroy() {
+    for (auto e : a) (void)hipEventDestroy(e);
+    for (auto e : b) (void)hipEventDestroy(e);
+    a.clear();
+    b.clear();
+  }
+};
+
 struct moe_cache_s {
+  Profiler prof;
   moe_shape shape;
   Dims d;
   Layout L;
@@ -274,6 +352,8 @@ moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t ma
 
 moe_status moe_cache_destroy(moe_cache c) {
   if (!c) return MOE_E_INVALID;
+  (void)c->prof.harvest_all();
+  c->prof.destroy();
   if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
   for (int g = 0; g < kMaxGroups; ++g)
     if (c->ev_fill[g]) (void)hipEventDestroy(c->ev_fill[g]);
@@ -307,7 +387,9 @@ moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t
   if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
   if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
+  hipError_t e = c->prof.timed(Profiler::ROUTE, s, [&] {
+    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
+  });
   if (e == hipSuccess) e = hipEventRecord(c->ev_plan, s);
   if (e != hipSuccess) return hip_fail(c, e);
   c->state = State::Planned;
@@ -325,7 +407,9 @@ moe_status moe_fill_misses(moe_cache c, int32_t groups, void* fill_stream) {
   // the victim slots.
   hipError_t e = hipStreamWaitEvent(s, c->ev_plan, 0);
   for (int g = 0; g < groups && e == hipSuccess; ++g) {
-    e = launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s);
+    e = c->prof.timed(Profiler::FILL, s, [&] {
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s);
+    });
     if (e == hipSuccess) e = hipEventRecord(c->ev_fill[g], s);
   }
   if (e != hipSuccess) return hip_fail(c, e);
@@ -342,20 +426,23 @@ moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
   if (T > 0 && (!x || !y || !aligned16(x) || ((uintptr_t)y & 3))) return MOE_E_INVALID;
   if (c->d.has_shared && T > 0 && (!shared_blob || !aligned16(shared_blob))) return MOE_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
+  auto& P = c->prof;
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
   const int G = c->fill_groups;
   hipError_t e = hipSuccess;
-  if (T > 0) {
-    e = launch_ffn_decode(c->d, c->v, x, c->arena, nullptr, 0, 0, 1, T, nu, s);
-    if (e == hipSuccess && c->d.has_shared)
-      e = launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, 2, 0, 1, T, 1, s);
-  }
+  if (T > 0)  // hit experts and the shared expert: no fill to wait for
+    e = P.timed(Profiler::FFN, s, [&] {
+      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 0, 0, 1, T,
+                               nu + c->d.has_shared, 0, s);
+    });
   for (int g = 0; g < G && e == hipSuccess; ++g) {
     e = hipStreamWaitEvent(s, c->ev_fill[g], 0);
     if (e == hipSuccess && T > 0)
-      e = launch_ffn_decode(c->d, c->v, x, c->arena, nullptr, 1, g, G, T, (nu + G - 1) / G, s);
+      e = P.timed(Profiler::FFN, s, [&] {
+        return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 1, g, G, T,
+                                 (nu + G - 1) / G, g == G - 1, s);
+      });
   }
-  if (e == hipSuccess && T > 0) e = launch_combine(c->d, c->v, y, T, c->d.has_shared, s);
   if (e != hipSuccess) return hip_fail(c, e);
   c->state = State::Idle;
   return MOE_OK;
@@ -439,6 +526,38 @@ moe_status moe_stats(moe_cache c, moe_counters* out) {
   out->hits = (int64_t)s[STAT_HITS];
   out->misses = (int64_t)s[STAT_MISSES];
   out->bytes_filled = (int64_t)s[STAT_BYTES];
+  return MOE_OK;
+}
+
+moe_status moe_profile_enable(moe_cache c, int32_t enable) {
+  if (!c) return MOE_E_INVALID;
+  hipError_t e = c->prof.harvest_all();
+  if (e == hipSuccess && enable) e = c->prof.ensure();
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess)
+    e = hipMemcpy(c->prof.stats0, c->v.stats, sizeof(c->prof.stats0), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  c->prof.reset();
+  c->prof.on = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_cache c, moe_profile* out) {
+  if (!c || !out) return MOE_E_INVALID;
+  hipError_t e = c->prof.harvest_all();
+  unsigned long long st[STAT_WORDS];
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(st, c->v.stats, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  const auto& P = c->prof;
+  out->route_launches = P.launches[Profiler::ROUTE];
+  out->fill_launches = P.launches[Profiler::FILL];
+  out->ffn_launches = P.launches[Profiler::FFN];
+  out->route_ms = P.ms[Profiler::ROUTE];
+  out->fill_ms = P.ms[Profiler::FILL];
+  out->ffn_ms = P.ms[Profiler::FFN];
+  out->fill_bytes = (int64_t)(st[STAT_BYTES] - P.stats0[STAT_BYTES]);
+  out->ffn_weight_bytes = (int64_t)(st[STAT_FFN_BYTES] - P.stats0[STAT_FFN_BYTES]);
   return MOE_OK;
 }
 

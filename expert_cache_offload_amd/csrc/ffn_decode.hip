@@ -1,4 +1,4 @@
-// SwiGLU expert FFN at decode: a weight-streaming GEMV over the cached expert blobs.
+// SwiGLU expert FFN at decode: weight-streaming GEMVs over the cached expert blobs.
 //
 // The pages give no expert form; the SwiGLU expert (FFN_e(x) = Wd (silu(Wg x) * (Wu x)))
 // is the one this library computes, summed over the top-k experts with the renormalised
@@ -8,21 +8,32 @@
 // misses runs as soon as its fill has landed ("FreeToken：在消费级 NVIDIA GPU 上进行 MoE
 // 推理", "FreeToken 解决的问题": one group computes while the next transfers).
 //
-// Gfx950 design: decode is HBM-bound (about one FLOP per weight byte), so every weight
-// byte is read once, coalesced, 16 bytes per lane.  A workgroup owns R consecutive
-// intermediate rows of one expert: it streams the gate|up rows (contiguous 2H elements
-// per row in the blob), forms a = silu(g) * u * w_token for each token routed to the
-// expert, then streams the same R rows of the stored down-projection transpose WdT and
-// writes an fp32 partial output row per (token, row block).  Every expert is read once
-// per step whatever number of tokens use it (cross-request sharing at batch > 1).
-// A combine kernel adds the partial rows of each token in a fixed order (deterministic)
-// and rounds to bf16.  Weight formats: bf16, fp8 e4m3fn with fp32 scale per 1x128 block,
-// MXFP4 (e2m1 with e8m0 scale per 32), decoded with gfx950's packed conversions.
+// Gfx950 design.  Decode is HBM-bound (about one FLOP per weight byte): every weight byte
+// is read once, in coalesced 16-byte lanes, with many loads in flight per wave.  Per group
+// of experts two streaming kernels run back to back, and the step ends with a combine:
+//   gate/up  - a workgroup owns 8 intermediate rows of one expert; each wave streams two
+//              gate|up rows (contiguous 2H elements each) with both rows' loads in flight,
+//              reduces across the wave, and writes a = silu(g) * u * w_token (fp32) for
+//              every token routed to the expert;
+//   down     - a workgroup owns a 128-byte-wide column block of the stored transpose WdT
+//              (64 bytes for MXFP4) and half or all of its rows; each thread streams a
+//              contiguous run of rows for 16 (8) bytes of columns, so no partial sums over
+//              the intermediate dimension leave the workgroup; it writes the expert's
+//              output columns (fp32);
+//   combine  - y[t] = bf16(sum over the token's k experts (+ shared) in a fixed order).
+// Kernel boundaries carry the dependencies: on gfx950 an agent-scope fence is an L2
+// write-back plus invalidate, far too costly per workgroup while fills stream into HBM.
+// The route kernel publishes a packed entry table (slot, token count, first row, miss
+// index) so a workgroup reaches its weights after two dependent loads.
+// Every expert is read once per step whatever number of tokens use it (cross-request
+// sharing at batch > 1).  fp8 e4m3fn and e2m1 are decoded with gfx950's packed conversions;
+// block scales are applied once per block of rows (down) or per 16-byte chunk (gate/up).
 #include "moe_dev.h"
 
 namespace moe {
 
 constexpr int FT = 256;  // threads per FFN workgroup (4 waves)
+constexpr int RA = 8;    // intermediate rows per gate/up workgroup (2 per wave)
 
 struct FfnArgs {
   Dims d;
@@ -30,48 +41,21 @@ struct FfnArgs {
   const uint16_t* x;  // [T][H] bf16
   const unsigned char* arena;
   const unsigned char* shared_blob;
-  int mode;  // 0: hit experts, 1: miss group `group` of `ngroups`, 2: shared expert
+  uint16_t* y;  // [T][H] bf16 (combine)
+  int sel;      // 0: hit experts + shared expert, 1: miss group `group` of `ngroups`
   int group;
   int ngroups;
   int T;
+  int NE;  // entry slots of this launch
+  int NC;  // combine workgroups (0 unless this is the step's last launch)
 };
 
 // ---- format helpers -------------------------------------------------------------
-template <int FMT>
-struct Fmt;
-
-template <>
-struct Fmt<FMT_BF16> {
-  static constexpr int EPL = 8;    // elements per 16 bytes
-  static constexpr int DCOLS = 8;  // down-projection columns per thread load
-  __device__ static size_t gu_row_bytes(int H) { return (size_t)2 * H * 2; }
-  __device__ static size_t d_row_bytes(int H) { return (size_t)H * 2; }
-  __device__ static size_t d_base(int H, int I) { return (size_t)4 * I * H; }
-  __device__ static void unpack(uint4 w, float* f) {
-    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
-  }
-  __device__ static void load_d(const unsigned char* p, float* f) { unpack(*(const uint4*)p, f); }
-};
-
 __device__ __forceinline__ void fp8x4(uint32_t v, float* f) {
   auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
   auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
   f[0] = lo[0]; f[1] = lo[1]; f[2] = hi[0]; f[3] = hi[1];
 }
-
-template <>
-struct Fmt<FMT_FP8> {
-  static constexpr int EPL = 16;
-  static constexpr int DCOLS = 16;
-  __device__ static size_t gu_row_bytes(int H) { return (size_t)2 * H; }
-  __device__ static size_t d_row_bytes(int H) { return (size_t)H; }
-  __device__ static size_t d_base(int H, int I) { return (size_t)2 * I * H; }
-  __device__ static void unpack(uint4 w, float* f) {
-    fp8x4(w.x, f); fp8x4(w.y, f + 4); fp8x4(w.z, f + 8); fp8x4(w.w, f + 12);
-  }
-  __device__ static void load_d(const unsigned char* p, float* f) { unpack(*(const uint4*)p, f); }
-};
 
 __device__ __forceinline__ void fp4x8(uint32_t v, float* f) {
   auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
@@ -82,13 +66,42 @@ __device__ __forceinline__ void fp4x8(uint32_t v, float* f) {
   f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
 }
 
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) { return __uint_as_float(c << 23); }
+
+template <int FMT>
+struct Fmt;
+
+template <>
+struct Fmt<FMT_BF16> {
+  static constexpr int EPL = 8;  // elements per 16 bytes
+  static constexpr int DC = 8;   // down-projection columns per thread load (16 bytes)
+  static constexpr int SB = 0;   // no scale blocks
+  __device__ static size_t row_bytes(int n) { return (size_t)n * 2; }
+  __device__ static void unpack(uint4 w, float* f) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+  }
+  __device__ static void load_d(const unsigned char* p, float* f) { unpack(*(const uint4*)p, f); }
+};
+
+template <>
+struct Fmt<FMT_FP8> {
+  static constexpr int EPL = 16;
+  static constexpr int DC = 16;  // 16 bytes
+  static constexpr int SB = 128;
+  __device__ static size_t row_bytes(int n) { return (size_t)n; }
+  __device__ static void unpack(uint4 w, float* f) {
+    fp8x4(w.x, f); fp8x4(w.y, f + 4); fp8x4(w.z, f + 8); fp8x4(w.w, f + 12);
+  }
+  __device__ static void load_d(const unsigned char* p, float* f) { unpack(*(const uint4*)p, f); }
+};
+
 template <>
 struct Fmt<FMT_MXFP4> {
   static constexpr int EPL = 32;
-  static constexpr int DCOLS = 16;  // 8-byte loads keep the accumulators in registers
-  __device__ static size_t gu_row_bytes(int H) { return (size_t)H; }
-  __device__ static size_t d_row_bytes(int H) { return (size_t)H / 2; }
-  __device__ static size_t d_base(int H, int I) { return (size_t)I * H; }
+  static constexpr int DC = 16;  // 8 bytes: keeps the down accumulators in registers
+  static constexpr int SB = 32;
+  __device__ static size_t row_bytes(int n) { return (size_t)n / 2; }
   __device__ static void unpack(uint4 w, float* f) {
     fp4x8(w.x, f); fp4x8(w.y, f + 8); fp4x8(w.z, f + 16); fp4x8(w.w, f + 24);
   }
@@ -99,9 +112,7 @@ struct Fmt<FMT_MXFP4> {
   }
 };
 
-__device__ __forceinline__ float e8m0_to_f32(uint32_t c) { return __uint_as_float(c << 23); }
-
-// Scale of the gate (g=0) or up (g=1) row i at contraction position xp.
+// Scale of gate (g=0) / up (g=1) row i at contraction position xp.
 template <int FMT>
 __device__ __forceinline__ float gu_scale(const unsigned char* blob, int H, int I, int i, int g,
                                           int xp) {
@@ -116,275 +127,396 @@ __device__ __forceinline__ float gu_scale(const unsigned char* blob, int H, int 
   }
 }
 
-// Scale of the down-projection block holding row i at column h.
+// Scales of the down-projection block `blk` for DC consecutive columns starting at c.
 template <int FMT>
-__device__ __forceinline__ float d_scale(const unsigned char* blob, int H, int I, int i, int h) {
+__device__ __forceinline__ void d_scales(const unsigned char* blob, int H, int I, int blk, int c,
+                                         float* sc) {
   if constexpr (FMT == FMT_FP8) {
-    const float* s = (const float*)(blob + (size_t)3 * I * H + (size_t)4 * 2 * I * (H / 128));
-    return s[(size_t)(i / 128) * H + h];
+    const float4* s = (const float4*)(blob + (size_t)3 * I * H + (size_t)4 * 2 * I * (H / 128) +
+                                      ((size_t)blk * H + c) * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = s[q];
+      sc[4 * q] = v.x; sc[4 * q + 1] = v.y; sc[4 * q + 2] = v.z; sc[4 * q + 3] = v.w;
+    }
   } else if constexpr (FMT == FMT_MXFP4) {
-    const unsigned char* s = blob + (size_t)3 * I * H / 2 + (size_t)2 * I * (H / 32);
-    return e8m0_to_f32(s[(size_t)(i / 32) * H + h]);
-  } else {
-    return 1.0f;
+    const uint4 a = *(const uint4*)(blob + (size_t)3 * I * H / 2 + (size_t)2 * I * (H / 32) +
+                                    (size_t)blk * H + c);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sc[q] = e8m0_to_f32((w[q / 4] >> (8 * (q % 4))) & 0xffu);
   }
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Launch selection -> entry index g in the step's order [hits, shared, misses].
+struct Entry {
+  int g;       // entry index
+  int ntok;
+  int row0;    // first act/yexp row (routed) or 0 (shared)
+  bool shared;
+  const unsigned char* blob;
+};
+
+__device__ __forceinline__ int n_entries_in_launch(const FfnArgs& a, int nHit, int nMiss,
+                                                   int& first) {
+  const int nHS = nHit + a.d.has_shared;
+  if (a.sel == 0) {  // hits and shared expert
+    first = 0;
+    return nHS;
+  }
+  const int m0 = (int)((long long)a.group * nMiss / a.ngroups);
+  const int m1 = (int)((long long)(a.group + 1) * nMiss / a.ngroups);
+  first = nHS + m0;
+  return m1 - m0;
+}
+
+__device__ __forceinline__ bool resolve(const FfnArgs& a, int j, Entry& en) {
+  const Dev& v = a.v;
+  const int nHit = v.hdr[HDR_NHIT], nMiss = v.hdr[HDR_NMISS];
+  int first;
+  const int n = n_entries_in_launch(a, nHit, nMiss, first);
+  if (j >= n) return false;
+  const int g = first + j;
+  en.g = g;
+  if (a.d.has_shared && g == nHit) {
+    en.shared = true;
+    en.ntok = a.T;
+    en.row0 = 0;
+    en.blob = a.shared_blob;
+    return true;
+  }
+  const int4 e = v.ent[g < nHit ? g : g - a.d.has_shared];
+  en.shared = false;
+  en.ntok = e.y;
+  en.row0 = e.z;
+  en.blob = a.arena + (size_t)e.x * (size_t)a.d.S;
+  return true;
+}
+
+// ---------------------------------------------------------------- gate / up role
 template <int FMT, int NTOK>
-__global__ __launch_bounds__(FT) void ffn_decode_kernel(FfnArgs a) {
+__device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb, unsigned char* smem) {
   using F = Fmt<FMT>;
   constexpr int EPL = F::EPL;
-  extern __shared__ __align__(16) unsigned char smem[];
   const Dims& d = a.d;
-  const Dev& v = a.v;
-  const int H = d.H, I = d.I, R = d.R;
-  const int j = blockIdx.x / d.nR, rb = blockIdx.x % d.nR;
+  const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-
-  __shared__ int s_tok[NTOK];
-  __shared__ float s_w[NTOK];
-  __shared__ int s_prow[NTOK];
-  int u = -1, ntok;
-  const unsigned char* blob;
-  if (a.mode == 2) {
-    if (j > 0) return;
-    blob = a.shared_blob;
-    ntok = a.T;
-  } else {
-    int n0, n1;
-    const int* list;
-    if (a.mode == 0) {
-      list = v.hit_list;
-      n0 = 0;
-      n1 = v.hdr[HDR_NHIT];
-    } else {
-      const int m = v.hdr[HDR_NMISS];
-      list = v.miss_list;
-      n0 = (int)((long long)a.group * m / a.ngroups);
-      n1 = (int)((long long)(a.group + 1) * m / a.ngroups);
-    }
-    if (j >= n1 - n0) return;
-    u = list[n0 + j];
-    blob = a.arena + (size_t)v.u_slot[u] * (size_t)d.S;
-    ntok = v.count[u];
-  }
-  if (ntok > NTOK) ntok = NTOK;  // host picks NTOK >= T
+  const int ntok = en.ntok < NTOK ? en.ntok : NTOK;
+  if (rb == 0 && threadIdx.x == 0)
+    atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
+  // two rows per wave: i0 = r0 + wave, i1 = r0 + wave + 4; their first chunks load before the
+  // activations are staged
+  const int i0 = rb * RA + wave, i1 = i0 + 4;
+  const size_t rbytes = F::row_bytes(2 * H);
+  const uint4* row0 = (const uint4*)(en.blob + (size_t)i0 * rbytes);
+  const uint4* row1 = (const uint4*)(en.blob + (size_t)i1 * rbytes);
+  const int nq = 2 * H / EPL;
+  int* s_tok = (int*)smem;              // [NTOK]
+  float* s_w = (float*)(s_tok + NTOK);  // [NTOK]
+  uint16_t* xs = (uint16_t*)(smem + 64);  // [NTOK][H]
   if ((int)threadIdx.x < ntok) {
     const int q = threadIdx.x;
-    if (u >= 0) {
-      const int pos = v.offset[u] + q;
-      const int asg = v.perm[pos];
-      s_tok[q] = asg / d.K;
-      s_w[q] = v.tk_w[asg];
-      s_prow[q] = pos;
-    } else {
-      s_tok[q] = q;
-      s_w[q] = 1.0f;
-      s_prow[q] = q;
-    }
+    s_tok[q] = en.shared ? q : a.v.row_tok[en.row0 + q];
+    s_w[q] = en.shared ? 1.0f : a.v.row_w[en.row0 + q];
   }
   __syncthreads();
-
-  // token activations -> LDS (bf16)
-  uint16_t* xs = (uint16_t*)smem;  // [NTOK][H]
-  float* as = (float*)(smem + (size_t)NTOK * H * 2);  // [NTOK][R]
   for (int q = 0; q < ntok; ++q) {
     const uint4* src = (const uint4*)(a.x + (size_t)s_tok[q] * H);
     uint4* dst = (uint4*)(xs + (size_t)q * H);
     for (int c = threadIdx.x; c < H / 8; c += FT) dst[c] = src[c];
   }
   __syncthreads();
-
-  const int r0 = rb * R;
-  // ---- gate / up: one wave per row, the row's 2H elements spread over the lanes ----
-  const int nq = 2 * H / EPL;
-  for (int rl = wave; rl < R; rl += FT / 64) {
-    const int i = r0 + rl;
-    const uint4* row = (const uint4*)(blob + (size_t)i * F::gu_row_bytes(H));
-    float accg[NTOK], accu[NTOK];
+  float g0[NTOK], u0[NTOK], g1[NTOK], u1[NTOK];
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t) accg[t] = accu[t] = 0.f;
+  for (int t = 0; t < NTOK; ++t) g0[t] = u0[t] = g1[t] = u1[t] = 0.f;
 #pragma unroll 4
-    for (int q = lane; q < nq; q += 64) {
-      const uint4 w = row[q];
-      const int p = q * EPL;
-      const bool isg = p < H;
-      const int xp = isg ? p : p - H;
-      float wf[EPL];
-      F::unpack(w, wf);
-      const float sc = gu_scale<FMT>(blob, H, I, i, isg ? 0 : 1, xp);
-#pragma unroll
-      for (int t = 0; t < NTOK; ++t) {
-        if (t < ntok) {
-          const uint4* xv = (const uint4*)(xs + (size_t)t * H + xp);
-          float dsum = 0.f;
-#pragma unroll
-          for (int c8 = 0; c8 < EPL / 8; ++c8) {
-            uint4 xx = xv[c8];
-            dsum += wf[c8 * 8 + 0] * bf16_lo(xx.x) + wf[c8 * 8 + 1] * bf16_hi(xx.x) +
-                    wf[c8 * 8 + 2] * bf16_lo(xx.y) + wf[c8 * 8 + 3] * bf16_hi(xx.y) +
-                    wf[c8 * 8 + 4] * bf16_lo(xx.z) + wf[c8 * 8 + 5] * bf16_hi(xx.z) +
-                    wf[c8 * 8 + 6] * bf16_lo(xx.w) + wf[c8 * 8 + 7] * bf16_hi(xx.w);
-          }
-          dsum *= sc;
-          accg[t] += isg ? dsum : 0.f;
-          accu[t] += isg ? 0.f : dsum;
-        }
-      }
-    }
+  for (int q = lane; q < nq; q += 64) {
+    const uint4 w0 = row0[q];
+    const uint4 w1 = row1[q];
+    const int p = q * EPL;
+    const bool isg = p < H;
+    const int xp = isg ? p : p - H;
+    float f0[EPL], f1[EPL];
+    F::unpack(w0, f0);
+    F::unpack(w1, f1);
+    const float s0 = gu_scale<FMT>(en.blob, H, I, i0, isg ? 0 : 1, xp);
+    const float s1 = gu_scale<FMT>(en.blob, H, I, i1, isg ? 0 : 1, xp);
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) {
       if (t < ntok) {
-        float g = accg[t], uu = accu[t];
-        for (int off = 32; off > 0; off >>= 1) {
-          g += __shfl_xor(g, off);
-          uu += __shfl_xor(uu, off);
+        const uint4* xv = (const uint4*)(xs + (size_t)t * H + xp);
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int c8 = 0; c8 < EPL / 8; ++c8) {
+          const uint4 xx = xv[c8];
+          const float xf[8] = {bf16_lo(xx.x), bf16_hi(xx.x), bf16_lo(xx.y), bf16_hi(xx.y),
+                               bf16_lo(xx.z), bf16_hi(xx.z), bf16_lo(xx.w), bf16_hi(xx.w)};
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            d0 += f0[c8 * 8 + c] * xf[c];
+            d1 += f1[c8 * 8 + c] * xf[c];
+          }
         }
-        if (lane == 0) as[t * R + rl] = silu(g) * uu * s_w[t];
+        d0 *= s0;
+        d1 *= s1;
+        if (isg) {
+          g0[t] += d0;
+          g1[t] += d1;
+        } else {
+          u0[t] += d0;
+          u1[t] += d1;
+        }
       }
     }
   }
-  __syncthreads();
+  float* act = en.shared ? a.v.act_shared : a.v.act;
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    if (t < ntok) {
+      float a0 = g0[t], b0 = u0[t], a1 = g1[t], b1 = u1[t];
+      for (int off = 32; off > 0; off >>= 1) {
+        a0 += __shfl_xor(a0, off);
+        b0 += __shfl_xor(b0, off);
+        a1 += __shfl_xor(a1, off);
+        b1 += __shfl_xor(b1, off);
+      }
+      if (lane == 0) {
+        float* out = act + (size_t)(en.row0 + t) * I;
+        out[i0] = silu(a0) * b0 * s_w[t];
+        out[i1] = silu(a1) * b1 * s_w[t];
+      }
+    }
+  }
+}
 
-  // ---- down projection: each thread owns DCOLS consecutive output columns ----
-  constexpr int DC = F::DCOLS;
-  const unsigned char* dbase = blob + F::d_base(H, I);
-  const size_t drow = F::d_row_bytes(H);
-  for (int c0 = threadIdx.x * DC; c0 < H; c0 += FT * DC) {
-    float acc[NTOK][DC];
+// ---------------------------------------------------------------- down role
+template <int FMT, int NTOK>
+__device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, unsigned char* smem) {
+  using F = Fmt<FMT>;
+  constexpr int DC = F::DC;
+  constexpr int HC = 8 * DC;  // columns per workgroup: 8 threads per row segment
+  const Dims& d = a.d;
+  const int H = d.H, I = d.I, RS = d.RS;
+  const int ntok = en.ntok < NTOK ? en.ntok : NTOK;
+  const int IR = I / RS;  // rows of this split
+  const int i_begin = rs * IR;
+  float* s_a = (float*)smem;               // [NTOK][IR]
+  float* s_red = s_a + (size_t)NTOK * IR;  // [4][NTOK][HC]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = threadIdx.x & 7, rl = threadIdx.x >> 3;  // column group, row lane (0..31)
+  const int c0 = cb * HC + cg * DC;
+  const int nrw = IR / 32;  // contiguous rows per thread
+  const int ra = i_begin + rl * nrw;
+  const unsigned char* wdt = en.blob + F::row_bytes(2 * H) * (size_t)I;  // WdT after Wgu
+  const size_t drow = F::row_bytes(H);
+  const size_t cbyte = F::row_bytes(c0);
+  const float* act = en.shared ? a.v.act_shared : a.v.act;
+  for (int q = 0; q < ntok; ++q)
+    for (int i = threadIdx.x; i < IR; i += FT)
+      s_a[q * IR + i] = act[(size_t)(en.row0 + q) * I + i_begin + i];
+  __syncthreads();
+  float acc[NTOK][DC];
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t)
+  for (int t = 0; t < NTOK; ++t)
 #pragma unroll
-      for (int c = 0; c < DC; ++c) acc[t][c] = 0.f;
-    const size_t col_byte = (size_t)c0 * drow / H;
-#pragma unroll 4
-    for (int rl = 0; rl < R; ++rl) {
-      float wf[DC];
-      F::load_d(dbase + (size_t)(r0 + rl) * drow + col_byte, wf);
+    for (int c = 0; c < DC; ++c) acc[t][c] = 0.f;
+
+  if constexpr (F::SB == 0) {
+#pragma unroll 8
+    for (int r = 0; r < nrw; ++r) {
+      const int i = ra + r;
+      float f[DC];
+      F::load_d(wdt + (size_t)i * drow + cbyte, f);
 #pragma unroll
       for (int t = 0; t < NTOK; ++t) {
         if (t < ntok) {
-          const float at = as[t * R + rl];
+          const float at = s_a[t * IR + (i - i_begin)];
 #pragma unroll
-          for (int c = 0; c < DC; ++c) acc[t][c] += at * wf[c];
+          for (int c = 0; c < DC; ++c) acc[t][c] += at * f[c];
         }
       }
     }
-    if constexpr (FMT != FMT_BF16) {
-      // R divides the scale block (128 for fp8, 32 for MXFP4): one scale per column
+  } else {
+    // rows of one scale block accumulate unscaled, then the block's column scales apply once
+    int r = 0;
+    while (r < nrw) {
+      const int i = ra + r;
+      const int blk = i / F::SB;
+      const int rend_blk = (blk + 1) * F::SB - ra;  // first r past this block
+      const int r1 = rend_blk < nrw ? rend_blk : nrw;
+      float bacc[NTOK][DC];
+#pragma unroll
+      for (int t = 0; t < NTOK; ++t)
+#pragma unroll
+        for (int c = 0; c < DC; ++c) bacc[t][c] = 0.f;
+#pragma unroll 4
+      for (; r < r1; ++r) {
+        const int ii = ra + r;
+        float f[DC];
+        F::load_d(wdt + (size_t)ii * drow + cbyte, f);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+          if (t < ntok) {
+            const float at = s_a[t * IR + (ii - i_begin)];
+#pragma unroll
+            for (int c = 0; c < DC; ++c) bacc[t][c] += at * f[c];
+          }
+        }
+      }
+      float sc[DC];
+      d_scales<FMT>(en.blob, H, I, blk, c0, sc);
+#pragma unroll
+      for (int t = 0; t < NTOK; ++t)
+#pragma unroll
+        for (int c = 0; c < DC; ++c) acc[t][c] += bacc[t][c] * sc[c];
+    }
+  }
+  // reduce over the 32 row lanes sharing a column group: 8 per wave by shuffles, 4 waves in LDS
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    if (t < ntok) {
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const float sc = d_scale<FMT>(blob, H, I, r0, c0 + c);
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) acc[t][c] *= sc;
-      }
-    }
-    float* outbase = (u >= 0) ? v.partial : v.shared_partial;
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) {
-      if (t < ntok) {
-        float4* o = (float4*)(outbase + ((size_t)s_prow[t] * d.nR + rb) * H + c0);
-#pragma unroll
-        for (int c = 0; c < DC; c += 4)
-          o[c / 4] = make_float4(acc[t][c], acc[t][c + 1], acc[t][c + 2], acc[t][c + 3]);
+        float s = acc[t][c];
+        s += __shfl_xor(s, 8);
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        acc[t][c] = s;
       }
     }
   }
+  if (lane < 8) {
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t)
+      if (t < ntok)
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+          s_red[((size_t)wave * NTOK + t) * HC + lane * DC + c] = acc[t][c];
+  }
+  __syncthreads();
+  float* yexp = en.shared ? a.v.yexp_shared : a.v.yexp;
+  for (int idx = threadIdx.x; idx < ntok * HC; idx += FT) {
+    const int t = idx / HC, c = idx % HC;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < FT / 64; ++w) s += s_red[((size_t)w * NTOK + t) * HC + c];
+    yexp[((size_t)(en.row0 + t) * RS + rs) * H + cb * HC + c] = s;
+  }
 }
 
-// ---- combine: y[t] = bf16( sum_j sum_r partial[pos(t,j)][r] + sum_r shared[t][r] ) ----
-constexpr int CT = 256;
-
-struct CombArgs {
-  Dims d;
-  Dev v;
-  uint16_t* y;
-  int T;
-  int with_shared;
-};
-
-__global__ __launch_bounds__(CT) void combine_kernel(CombArgs a) {
+// ---------------------------------------------------------------- combine role
+// y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + sum_rs yexp_shared[t][rs] ), fixed order.
+__device__ void combine_role(const FfnArgs& a, int cblk) {
   const Dims& d = a.d;
   const Dev& v = a.v;
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = blockIdx.y * 64 + lane;
-  const int nrow = d.K * d.nR + (a.with_shared ? d.nR : 0);
-  float s = 0.f;
-  for (int rho = wave; rho < nrow; rho += CT / 64) {
-    const float* src;
-    if (rho < d.K * d.nR) {
-      const int jj = rho / d.nR, r = rho % d.nR;
-      const int pos = v.inv_pos[t * d.K + jj];
-      src = v.partial + ((size_t)pos * d.nR + r) * d.H;
-    } else {
-      const int r = rho - d.K * d.nR;
-      src = v.shared_partial + ((size_t)t * d.nR + r) * d.H;
-    }
-    s += src[c];
-  }
-  __shared__ float red[CT / 64][64];
-  red[wave][lane] = s;
+  const int per_tok = (d.H + FT - 1) / FT;
+  const int t = cblk / per_tok;
+  const int c = (cblk % per_tok) * FT + threadIdx.x;
+  __shared__ int s_pos[32];
+  if ((int)threadIdx.x < d.K) s_pos[threadIdx.x] = v.inv_pos[t * d.K + threadIdx.x];
   __syncthreads();
-  if (wave == 0) {
-    float tot = red[0][lane];
-    for (int w = 1; w < CT / 64; ++w) tot += red[w][lane];
-    a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(tot);
-  }
-}
-
-size_t ffn_decode_lds_bytes(const Dims& d, int ntok) {
-  return (size_t)ntok * d.H * 2 + sizeof(float) * (size_t)ntok * d.R;
-}
-
-template <int FMT, int NTOK>
-static hipError_t launch_one(const FfnArgs& a, int grid, hipStream_t s) {
-  const size_t lds = ffn_decode_lds_bytes(a.d, NTOK);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)ffn_decode_kernel<FMT, NTOK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((ffn_decode_kernel<FMT, NTOK>), dim3(grid), dim3(FT), lds, s, a);
-  return hipGetLastError();
+  if (c >= d.H) return;
+  float s = 0.f;
+  for (int jj = 0; jj < d.K; ++jj)
+    for (int rs = 0; rs < d.RS; ++rs) s += v.yexp[((size_t)s_pos[jj] * d.RS + rs) * d.H + c];
+  if (d.has_shared)
+    for (int rs = 0; rs < d.RS; ++rs) s += v.yexp_shared[((size_t)t * d.RS + rs) * d.H + c];
+  a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
 }
 
 template <int FMT>
-static hipError_t launch_fmt(const FfnArgs& a, int ntok, int grid, hipStream_t s) {
-  switch (ntok) {
-    case 1: return launch_one<FMT, 1>(a, grid, s);
-    case 2: return launch_one<FMT, 2>(a, grid, s);
-    case 4: return launch_one<FMT, 4>(a, grid, s);
-    default: return launch_one<FMT, 8>(a, grid, s);
-  }
+static constexpr int down_hc() {
+  return 8 * Fmt<FMT>::DC;
 }
+
+template <int FMT, int NTOK>
+__global__ __launch_bounds__(FT) void ffn_gate_up_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nra = a.d.I / RA;
+  Entry en;
+  if (!resolve(a, blockIdx.x / nra, en)) return;
+  gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra, smem);
+}
+
+template <int FMT, int NTOK>
+__global__ __launch_bounds__(FT) void ffn_down_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Dims& d = a.d;
+  const int ndn = (d.H / down_hc<FMT>()) * d.RS;
+  Entry en;
+  if (!resolve(a, blockIdx.x / ndn, en)) return;
+  const int r = blockIdx.x % ndn;
+  down_role<FMT, NTOK>(a, en, r / d.RS, r % d.RS, smem);
+}
+
+__global__ __launch_bounds__(FT) void combine_kernel(FfnArgs a) { combine_role(a, blockIdx.x); }
 
 int decode_ntok(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
-// mode 0: hits, 1: miss group, 2: shared.  max_entries bounds the workgroups launched.
-hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
-                             const void* shared_blob, int mode, int group, int ngroups, int T,
-                             int max_entries, hipStream_t s) {
-  if (max_entries <= 0) return hipSuccess;
-  FfnArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
-            (const unsigned char*)shared_blob, mode, group, ngroups, T};
-  const int ntok = decode_ntok(T);
-  const int grid = max_entries * d.nR;
-  switch (d.fmt) {
-    case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, grid, s);
-    case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, grid, s);
-    default: return launch_fmt<FMT_MXFP4>(a, ntok, grid, s);
+template <class Kern>
+static hipError_t launch_with_lds(Kern kernel, int grid, size_t lds, const FfnArgs& a,
+                                  hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(FT), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int NTOK>
+static hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+  const Dims& d = a.d;
+  constexpr int HC = down_hc<FMT>();
+  hipError_t e = launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA),
+                                 64 + (size_t)NTOK * d.H * 2, a, s);
+  if (e != hipSuccess) return e;
+  e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
+                      sizeof(float) * ((size_t)NTOK * (d.I / d.RS) + (size_t)4 * NTOK * HC), a,
+                      s);
+  if (e != hipSuccess) return e;
+  if (a.NC > 0) {
+    hipLaunchKernelGGL(combine_kernel, dim3(a.NC), dim3(FT), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const FfnArgs& a, int ntok, hipStream_t s) {
+  switch (ntok) {
+    case 1: return launch_ffn<FMT, 1>(a, s);
+    case 2: return launch_ffn<FMT, 2>(a, s);
+    case 4: return launch_ffn<FMT, 4>(a, s);
+    default: return launch_ffn<FMT, 8>(a, s);
   }
 }
 
-hipError_t launch_combine(const Dims& d, const Dev& v, void* y, int T, int with_shared,
-                          hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  CombArgs a{d, v, (uint16_t*)y, T, with_shared};
-  hipLaunchKernelGGL(combine_kernel, dim3(T, d.H / 64), dim3(CT), 0, s, a);
-  return hipGetLastError();
+int down_columns_per_block(int fmt) {
+  return fmt == FMT_BF16 ? down_hc<FMT_BF16>()
+                         : fmt == FMT_FP8 ? down_hc<FMT_FP8>() : down_hc<FMT_MXFP4>();
+}
+
+// sel 0: hit experts and the shared expert; sel 1: miss group `group` of `ngroups`.
+// max_entries bounds the entries of the launch; with_combine adds the combine kernel after
+// it (only on the step's last launch).
+hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
+                             const void* shared_blob, void* y, int sel, int group, int ngroups,
+                             int T, int max_entries, int with_combine, hipStream_t s) {
+  const int nc = with_combine ? T * ((d.H + FT - 1) / FT) : 0;
+  FfnArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
+            (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
+            max_entries > 0 ? max_entries : 0, nc};
+  const int ntok = decode_ntok(T);
+  switch (d.fmt) {
+    case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, s);
+    case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, s);
+    default: return launch_fmt<FMT_MXFP4>(a, ntok, s);
+  }
 }
 
 }  // namespace moe

@@ -33,6 +33,7 @@ struct FillArgs {
 };
 
 constexpr int FILL_THREADS = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(FILL_THREADS) void fill_kernel(FillArgs a) {
   const int m = a.v.hdr[HDR_NMISS];
@@ -54,7 +55,8 @@ __global__ __launch_bounds__(FILL_THREADS) void fill_kernel(FillArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const size_t k = i + q * nthr;
-        if (k < S16) dst[k] = r[q];
+        // streaming store: the blob is read by the FFN later, not by this kernel
+        if (k < S16) __builtin_nontemporal_store(*(const u32x4*)&r[q], (u32x4*)(dst + k));
       }
     }
   }

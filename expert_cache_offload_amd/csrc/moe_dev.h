@@ -9,7 +9,7 @@
 // Per-step plan (rewritten by every route launch):
 //   hdr[16], U/u_slot/u_hit/hit_list/miss_list/miss_key/miss_slot/miss_victim[umax],
 //   count[umax], offset[umax+1], perm/inv_pos/tk_idx/tk_w[amax], logits[max_tokens*E],
-//   FFN partial sums.
+//   FFN intermediates (act) and per-expert outputs (yexp).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,7 +36,14 @@ enum : int {
   HDR_WORDS = 16
 };
 enum : int { ERR_CAPACITY = 1 };
-enum : int { STAT_STEPS = 0, STAT_HITS = 1, STAT_MISSES = 2, STAT_BYTES = 3, STAT_WORDS = 4 };
+enum : int {
+  STAT_STEPS = 0,
+  STAT_HITS = 1,
+  STAT_MISSES = 2,
+  STAT_BYTES = 3,
+  STAT_FFN_BYTES = 4,
+  STAT_WORDS = 8
+};
 
 constexpr int FMT_BF16 = 0, FMT_FP8 = 1, FMT_MXFP4 = 2;
 constexpr int kDecodeMaxTokens = 8;  // T handled by the GEMV decode path
@@ -46,8 +53,7 @@ struct Dims {
   int umax;          // min(max_tokens*K, E): distinct experts per step
   int amax;          // max_tokens*K: (token, choice) assignments per step
   int max_capacity;  // slots the arena holds
-  int R;             // intermediate rows per FFN workgroup
-  int nR;            // I / R
+  int RS;            // row splits of the down projection (1 or 2)
   long long S;       // blob bytes
 };
 
@@ -73,10 +79,17 @@ struct Dev {
   int* tk_idx;
   float* tk_w;
   double* logits;
-  float* partial;         // [amax * nR][H] routed partial outputs (decode path)
-  float* shared_partial;  // [max_tokens * nR][H] shared-expert partial outputs
-  int* moves;             // [max_capacity * 2] resize moves (src, dst)
+  float* act;          // [amax][I] silu(g)*u*w per (expert, token) row
+  float* act_shared;   // [max_tokens][I] shared expert
+  float* yexp;         // [amax][RS][H] per (expert, token) output
+  float* yexp_shared;  // [max_tokens][RS][H] shared expert
+  int4* ent;           // [umax] FFN entries in order hits, misses: {slot, ntok, row0, miss idx}
+  int* row_tok;        // [amax] token of each expert-sorted assignment row
+  float* row_w;        // [amax] routing weight of each row
+  int* moves;          // [max_capacity * 2] resize moves (src, dst)
 };
+
+constexpr int kMaxFillGroups = 64;
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }

@@ -11,7 +11,8 @@
 // (one expert row per wave, fp64 accumulation of exact bf16 x bf16 products so near
 // ties are ordered as in exact arithmetic); the last workgroup to arrive (an
 // agent-scope ticket) then runs the whole plan in LDS:
-//   top-k per token (wave argmax, ties to the lower expert id) and renormalised softmax;
+//   top-k per token by rank counting over the LDS-resident logits (ties to the lower
+//   expert id; every (token, expert) pair ranked in parallel) and renormalised softmax;
 //   dedup by an LDS histogram and a wave-ballot / popcount prefix that yields the
 //   distinct experts U already ascending;
 //   hit/miss classification against slot_of;
@@ -115,8 +116,11 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   }
 
   // ---------------- ticket: the last workgroup plans ----------------
+  // Each wave's logit stores complete (workgroup-scope release: a wait, no cache action);
+  // one agent-scope release per workgroup publishes them before its ticket, and the last
+  // workgroup's single acquire makes every workgroup's logits visible to it.
   __shared__ int s_last;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   if (threadIdx.x == 0) {
     int prev = __hip_atomic_fetch_add(&v.ctrl[CTRL_TICKET], 1, __ATOMIC_ACQ_REL,
@@ -125,7 +129,6 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   // ---------------- phase B (one workgroup) ----------------
   const int A = T * K;
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   // LDS carve-up
   unsigned char* p = smem;
   uint64_t* s_comp = (uint64_t*)p;  p += sizeof(uint64_t) * d.max_capacity;
+  double* s_z = (double*)p;         p += sizeof(double) * (size_t)d.max_tokens * E;
   int* s_cnt = (int*)p;             p += sizeof(int) * E;
   int* s_uidx = (int*)p;            p += sizeof(int) * E;
   int* s_tk_idx = (int*)p;          p += sizeof(int) * d.amax;
@@ -148,6 +152,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   int* s_sorted = (int*)p;          p += sizeof(int) * umax;
   int* s_aslot = (int*)p;           p += sizeof(int) * umax;
   int* s_avkey = (int*)p;           p += sizeof(int) * umax;
+  int* s_hitl = (int*)p;            p += sizeof(int) * umax;
   __shared__ int s_tmp[8];
   __shared__ uint64_t s_tmp64[8];
   __shared__ int s_g;
@@ -157,49 +162,36 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     s_uidx[e] = -1;
   }
 
-  // top-k per token: one wave per token, E/64 logits per lane
-  for (int t = wave; t < T; t += RT / 64) {
-    double z[16];
-    const int nch = (E + 63) / 64;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      int e = c * 64 + lane;
-      z[c] = (c < nch && e < E) ? v.logits[(size_t)t * E + e] : -__builtin_huge_val();
+  // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
+  // the experts of rank < K are the selection, in order.  NaN logits count as -inf so the
+  // ranks stay a permutation.
+  for (int i = threadIdx.x; i < T * E; i += RT) {
+    const double z = v.logits[i];
+    s_z[i] = (z == z) ? z : -__builtin_huge_val();
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * E; i += RT) {
+    const int t = i / E, e = i - t * E;
+    const double z = s_z[i];
+    const double* zt = s_z + (size_t)t * E;
+    int rank = 0;
+    for (int e2 = 0; e2 < E; ++e2) {
+      const double z2 = zt[e2];
+      rank += (z2 > z) || (z2 == z && e2 < e);
     }
-    uint32_t taken = 0;
-    for (int j = 0; j < K; ++j) {
-      double bv = -__builtin_huge_val();
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        int e = c * 64 + lane;
-        if (c < nch && e < E && !((taken >> c) & 1u) && (z[c] > bv || bi == 0x7fffffff)) {
-          if (z[c] > bv || bi == 0x7fffffff) {
-            bv = z[c];
-            bi = e;
-          }
-        }
-      }
-      for (int off = 32; off > 0; off >>= 1) {
-        double ov = __shfl_xor(bv, off);
-        int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) {
-        s_tk_idx[t * K + j] = bi;
-        s_tk_z[t * K + j] = bv;
-      }
+    if (rank < K) {
+      s_tk_idx[t * K + rank] = e;
+      s_tk_z[t * K + rank] = z;
     }
-    if (lane == 0) {
-      double z0 = s_tk_z[t * K];
-      double sum = 0.0;
-      for (int j = 0; j < K; ++j) sum += exp(s_tk_z[t * K + j] - z0);
-      for (int j = 0; j < K; ++j) s_tk_w[t * K + j] = (float)(exp(s_tk_z[t * K + j] - z0) / sum);
-    }
+  }
+  __syncthreads();
+  // renormalised softmax over the selected logits (differences in fp64, exp in fp32)
+  for (int i = threadIdx.x; i < A; i += RT) {
+    const int t = i / K;
+    const double z0 = s_tk_z[t * K];
+    float sum = 0.f;
+    for (int jj = 0; jj < K; ++jj) sum += expf((float)(s_tk_z[t * K + jj] - z0));
+    s_tk_w[i] = expf((float)(s_tk_z[i] - z0)) / sum;
   }
   __syncthreads();
 
@@ -244,6 +236,8 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     int pos = s_off[s_uidx[e]] + rank;
     v.perm[pos] = i;
     v.inv_pos[i] = pos;
+    v.row_tok[pos] = i / K;
+    v.row_w[pos] = s_tk_w[i];
   }
 
   // classification
@@ -255,7 +249,11 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   }
   __syncthreads();
   const int nHit = block_compact(
-      nU, [&](int u) { return s_hit[u] != 0; }, [&](int u, int pos) { v.hit_list[pos] = u; },
+      nU, [&](int u) { return s_hit[u] != 0; },
+      [&](int u, int pos) {
+        v.hit_list[pos] = u;
+        s_hitl[pos] = u;
+      },
       s_tmp);
   const int nMiss = block_compact(
       nU, [&](int u) { return s_hit[u] == 0; },
@@ -276,11 +274,11 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   if (threadIdx.x == 0) s_err = 0;
   if (need > 0) {
     const uint64_t NONE = ~0ull;
-    for (int i = threadIdx.x; i < n; i += RT) {
-      int k = v.key_of[i];
-      bool in_step = (k / E == layer) && s_uidx[k % E] >= 0;
-      s_comp[i] = in_step ? NONE : (((uint64_t)(uint32_t)v.stamp[i] << 32) | (uint32_t)k);
-    }
+    for (int i = threadIdx.x; i < n; i += RT)
+      s_comp[i] = ((uint64_t)(uint32_t)v.stamp[i] << 32) | (uint32_t)v.key_of[i];
+    __syncthreads();
+    for (int u = threadIdx.x; u < nU; u += RT)  // keys of this step are never victims
+      if (s_hit[u]) s_comp[s_uslot[u]] = NONE;
     __syncthreads();
     int got = 0;
     for (int round = 0; round < need && got < need; ++round) {
@@ -358,6 +356,12 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     v.u_slot[u] = s_uslot[u];
     v.u_hit[u] = s_hit[u];
   }
+  // FFN entry table: hits first, then misses in ascending expert id (the fill order)
+  for (int g = threadIdx.x; g < nU; g += RT) {
+    const int miss = g < nHit ? -1 : g - nHit;
+    const int u = miss < 0 ? s_hitl[g] : s_miss[miss];
+    v.ent[g] = make_int4(s_uslot[u], s_cnt[s_U[u]], s_off[u], miss);
+  }
   if (threadIdx.x == 0) {
     int nn = n + nMiss;
     v.ctrl[CTRL_N] = nn < C ? nn : C;
@@ -381,9 +385,10 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
 
 size_t route_plan_lds_bytes(const Dims& d) {
   size_t b = sizeof(uint64_t) * (size_t)d.max_capacity;
+  b += sizeof(double) * (size_t)d.max_tokens * d.E;
   b += sizeof(int) * 2 * (size_t)d.E;
   b += (sizeof(int) + sizeof(float) + sizeof(double)) * (size_t)d.amax;
-  b += sizeof(int) * (size_t)(10 * d.umax + 1);
+  b += sizeof(int) * (size_t)(11 * d.umax + 1);
   return (b + 15) & ~(size_t)15;
 }
 

@@ -28,7 +28,8 @@ def pinned_view(addr: int, nbytes: int) -> np.ndarray:
 
 class Workbench:
     def __init__(self, wl, device: str = "cuda:0", groups: int = 2, capacity: int | None = None,
-                 max_capacity: int | None = None, gen_threads: int = 0, token_steps=None):
+                 max_capacity: int | None = None, gen_threads: int = 0, token_steps=None,
+                 compute_stream=None, fill_stream=None):
         self.wl = wl
         self.dev = torch.device(device)
         self.groups = groups
@@ -67,8 +68,8 @@ class Workbench:
         self.y = torch.zeros((L, self.T, H), dtype=torch.int16, device=self.dev)
         self.topk_idx = torch.zeros((L, self.T, K), dtype=torch.int32, device=self.dev)
         self.topk_w = torch.zeros((L, self.T, K), dtype=torch.float32, device=self.dev)
-        self.compute = torch.cuda.Stream(device=self.dev)
-        self.fill = torch.cuda.Stream(device=self.dev)
+        self.compute = compute_stream or torch.cuda.Stream(device=self.dev)
+        self.fill = fill_stream or torch.cuda.Stream(device=self.dev)
         torch.cuda.synchronize(self.dev)
         self.handle = moe_cache_create(self.shape, self.capacity, self.max_capacity, self.arena,
                                        self.ws, self.pool_addr, self.compute.cuda_stream)

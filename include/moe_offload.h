@@ -188,6 +188,21 @@ moe_status moe_plan_read(moe_cache cache, moe_plan_host* out);
 /* Synchronous read of the device-side counters. */
 moe_status moe_stats(moe_cache cache, moe_counters* out);
 
+/* Per-kernel timing of the library's own launches, for measurement.  When enabled,
+ * every route, fill and FFN launch is bracketed by a pair of timing events on the
+ * stream it runs on (eager calls only: do not enable while a stream is captured).
+ * moe_profile_enable resets the accumulators; moe_profile_read synchronises.
+ * ffn_weight_bytes counts the expert-weight bytes the FFN kernels were given
+ * (each processed expert blob once), i.e. the algorithmic bytes of the FFN. */
+typedef struct {
+  int64_t route_launches, fill_launches, ffn_launches;
+  double route_ms, fill_ms, ffn_ms;
+  int64_t fill_bytes, ffn_weight_bytes;
+} moe_profile;
+
+moe_status moe_profile_enable(moe_cache cache, int32_t enable);
+moe_status moe_profile_read(moe_cache cache, moe_profile* out);
+
 const char* moe_status_string(moe_status s);
 
 /* The hipError_t of the last MOE_E_HIP returned on this handle (0 if none). */
