@@ -8,10 +8,13 @@ pinned host pool (58 GB), one LRU slot cache shared by all layers holding 30% of
 decode token through all 48 layer steps (route, dedup, classify, LRU, fills, FFN).  The
 first --warmup tokens are untimed; exactly --steps tokens are timed.
 
-Reported (one JSON line): decode tokens/s of the stack; the FFN weight-streaming kernel
-against the MI355X HBM roofline (achieved = expert-weight bytes the FFN kernels were given
-/ their event-measured duration); fill bandwidth against pinned hipMemcpyAsync H2D measured
-on the same box; the float64 CPU oracle on a bounded sample of the same workload.
+Reported (one JSON line): decode tokens/s of the stack; the dominant FFN kernel (the
+gate/up weight-streaming kernel, two thirds of the expert bytes) against the MI355X HBM
+roofline - achieved = the expert-weight bytes it was given / its launch durations, timed
+with event pairs on the compute stream over the timed tokens; fill bandwidth against pinned
+hipMemcpyAsync H2D measured on the same box; the float64 CPU oracle on a bounded sample of
+the same workload.  A short untimed pass after the timed tokens times the other kernels
+(route/plan, fill, down) for the breakdown.
 """
 from __future__ import annotations
 
@@ -90,6 +93,12 @@ def cpu_baseline(wb, tokens: int) -> dict:
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
+def _with_cache_frac(wl, frac: float):
+    import dataclasses
+    return dataclasses.replace(wl, name=f"{wl.name}_cache{frac:g}", cache_frac=frac,
+                               fixed_capacity=0)
+
+
 def _ffn_source_hash() -> str:
     here = os.path.dirname(os.path.abspath(__file__))
     p = os.path.join(here, "expert_cache_offload_amd", "csrc", "ffn_decode.hip")
@@ -97,7 +106,7 @@ def _ffn_source_hash() -> str:
 
 
 def _traffic_from_profile(name: str) -> float | None:
-    """HBM bytes per FFN launch from a committed counter summary, if it was taken on the
+    """HBM bytes per gate/up launch from a committed counter summary, if it was taken on the
     current kernel source (its header line records the source hash)."""
     here = os.path.dirname(os.path.abspath(__file__))
     p = os.path.join(here, "profiles", name)
@@ -109,7 +118,7 @@ def _traffic_from_profile(name: str) -> float | None:
     for line in open(p):
         if line.startswith("ffn_source_sha256_16:") and line.split(":", 1)[1].strip() == h:
             src_ok = True
-        if line.startswith("hbm_bytes_per_ffn_launch:"):
+        if line.startswith("hbm_bytes_per_launch:"):
             val = float(line.split(":", 1)[1])
     return val if src_ok else None
 
@@ -121,7 +130,14 @@ def main() -> None:
     ap.add_argument("--warmup", type=int, default=32, help="untimed decode tokens before")
     ap.add_argument("--workload", default="qwen35b_decode")
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0 = workload's)")
-    ap.add_argument("--groups", type=int, default=2, help="fill groups per step")
+    ap.add_argument("--groups", type=int, default=0,
+                    help="fill groups per step on a side stream (0: whole step on one stream)")
+    ap.add_argument("--profile-every", type=int, default=8,
+                    help="time one gate/up launch in this many during the timed region")
+    ap.add_argument("--cache-frac", type=float, default=0.0,
+                    help="override the cache fraction (1.0: every expert fits, FFN alone)")
+    ap.add_argument("--breakdown-steps", type=int, default=16,
+                    help="untimed tokens after the timed region with every kernel timed")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="oracle sample (token steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events")
@@ -133,21 +149,25 @@ def main() -> None:
     import torch
 
     import moe_inputs as mi
-    from expert_cache_offload_amd import moe_profile_enable, moe_profile_read
+    from expert_cache_offload_amd import (PROF_ALL, PROF_GATE_UP, moe_profile_enable,
+                                          moe_profile_read)
     from expert_cache_offload_amd.runner import Workbench
 
     wl = mi.WORKLOADS[args.workload]
     if args.layers:
         wl = wl.with_layers(args.layers)
+    if args.cache_frac > 0:
+        wl = _with_cache_frac(wl, args.cache_frac)
     n_tok = args.warmup + args.steps
+    n_all = n_tok + args.breakdown_steps
     if wl.kind != "decode":
         raise SystemExit("bench.py times decode workloads")
-    wl = wl.with_steps(max(n_tok, args.cpu_tokens))
+    wl = wl.with_steps(max(n_all, args.cpu_tokens))
     print(f"[bench] workload {wl.name}: L={wl.layers} H={wl.hidden} E={wl.experts} k={wl.top_k} "
           f"I={wl.inter} fmt={wl.fmt} C={wl.capacity} pool={wl.pool_bytes / 1e9:.2f} GB",
           file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    wb = Workbench(wl, groups=args.groups)
+    wb = Workbench(wl, groups=args.groups, max_capacity=wl.capacity)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     L = wl.layers
     for t in range(args.warmup):
@@ -156,7 +176,7 @@ def main() -> None:
     wb.sync()
     st0 = wb.stats()
     if not args.no_profile:
-        moe_profile_enable(wb.handle, True)
+        moe_profile_enable(wb.handle, PROF_GATE_UP, args.profile_every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(args.warmup, n_tok):
@@ -167,6 +187,14 @@ def main() -> None:
     wall = t1 - t0
     prof = moe_profile_read(wb.handle) if not args.no_profile else None
     st1 = wb.stats()
+    brk = None
+    if not args.no_profile and args.breakdown_steps > 0:
+        moe_profile_enable(wb.handle, PROF_ALL)
+        for t in range(n_tok, n_all):
+            for l in range(L):
+                wb.step(t, l)
+        brk = moe_profile_read(wb.handle)
+        moe_profile_enable(wb.handle, 0)
     hits = st1["hits"] - st0["hits"]
     misses = st1["misses"] - st0["misses"]
     fill_bytes = st1["bytes_filled"] - st0["bytes_filled"]
@@ -185,25 +213,34 @@ def main() -> None:
     roofline = None
     fill = {"bytes": fill_bytes, "link_GBps": fill_bytes / wall / 1e9,
             "h2d_memcpy_blob_GBps": h2d["blob_GBps"], "h2d_memcpy_1GiB_GBps": h2d["large_GBps"]}
+    extra = {}
     if prof is not None:
-        ffn_bytes = prof["ffn_weight_bytes"]
-        ffn_s = prof["ffn_ms"] / 1e3
-        achieved = ffn_bytes / ffn_s / 1e9 if ffn_s > 0 else 0.0
-        traffic = _traffic_from_profile(f"ffn_decode_{wl.name}_pmc.txt")
+        gu = prof["gate_up"]
+        gu_bytes = prof["gate_up_timed_bytes"]  # expert bytes the timed launches were given
+        gu_s = gu["ms"] / 1e3
+        achieved = gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0
+        traffic = _traffic_from_profile(f"ffn_gate_up_{wl.name}_pmc.txt")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "kernel": "ffn_kernel",
-                    "launches": prof["ffn_launches"],
-                    "avg_launch_us": round(prof["ffn_ms"] * 1e3 / max(1, prof["ffn_launches"]), 2),
-                    "algorithmic_bytes_per_launch": ffn_bytes / max(1, prof["ffn_launches"])}
-        fill_kernel_gbps = prof["fill_bytes"] / (prof["fill_ms"] / 1e3) / 1e9 if prof["fill_ms"] else 0
+                    "traffic": traffic, "kernel": "ffn_gate_up_kernel",
+                    "launches": gu["launches"],
+                    "avg_launch_us": round(gu["ms"] * 1e3 / max(1, gu["launches"]), 3),
+                    "algorithmic_bytes_per_launch": round(gu_bytes / max(1, gu["launches"]))}
+    if brk is not None:
+        nb = args.breakdown_steps
+        per = lambda k: round(brk[k]["ms"] * 1e3 / max(1, brk[k]["launches"]), 2)  # noqa: E731
+        fk = brk["fill"]
+        fill_kernel_gbps = brk["fill_bytes"] / (fk["ms"] / 1e3) / 1e9 if fk["ms"] else 0.0
         fill.update({"kernel_GBps": round(fill_kernel_gbps, 2),
-                     "kernel_frac_of_memcpy": round(fill_kernel_gbps / h2d["blob_GBps"], 3),
-                     "fill_launches": prof["fill_launches"],
-                     "link_busy_frac": round(prof["fill_ms"] / 1e3 / wall, 3)})
-        extra = {"route_us": round(prof["route_ms"] * 1e3 / max(1, prof["route_launches"]), 2)}
-    else:
-        extra = {}
+                     "kernel_frac_of_memcpy": round(fill_kernel_gbps / h2d["blob_GBps"], 3)})
+        extra["breakdown"] = {
+            "tokens": nb, "note": "untimed tokens after the timed region, every launch timed",
+            "route_us_per_launch": per("route"), "fill_us_per_launch": per("fill"),
+            "gate_up_us_per_launch": per("gate_up"), "down_us_per_launch": per("down"),
+            "route_ms_per_token": round(brk["route"]["ms"] / nb, 3),
+            "fill_ms_per_token": round(fk["ms"] / nb, 3),
+            "gate_up_ms_per_token": round(brk["gate_up"]["ms"] / nb, 3),
+            "down_ms_per_token": round(brk["down"]["ms"] / nb, 3)}
     fill["link_frac_of_memcpy"] = round(fill["link_GBps"] / h2d["blob_GBps"], 3)
 
     cpu = None

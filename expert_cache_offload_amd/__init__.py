@@ -56,10 +56,14 @@ class MoeCounters(ctypes.Structure):
 
 
 class MoeProfile(ctypes.Structure):
-    _fields_ = [("route_launches", ctypes.c_int64), ("fill_launches", ctypes.c_int64),
-                ("ffn_launches", ctypes.c_int64), ("route_ms", ctypes.c_double),
-                ("fill_ms", ctypes.c_double), ("ffn_ms", ctypes.c_double),
-                ("fill_bytes", ctypes.c_int64), ("ffn_weight_bytes", ctypes.c_int64)]
+    _fields_ = [("launches", ctypes.c_int64 * 4), ("ms", ctypes.c_double * 4),
+                ("fill_bytes", ctypes.c_int64), ("ffn_weight_bytes", ctypes.c_int64),
+                ("gate_up_timed_bytes", ctypes.c_int64)]
+
+
+PROF_ROUTE, PROF_FILL, PROF_GATE_UP, PROF_DOWN = 1, 2, 4, 8
+PROF_ALL = 15
+_PROF_KINDS = ("route", "fill", "gate_up", "down")
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -79,7 +83,7 @@ _SIGS = {
     "moe_cache_snapshot": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_plan_read": (_i32, [_vp, ctypes.POINTER(MoePlanHost)]),
     "moe_stats": (_i32, [_vp, ctypes.POINTER(MoeCounters)]),
-    "moe_profile_enable": (_i32, [_vp, _i32]),
+    "moe_profile_enable": (_i32, [_vp, _i32, _i32]),
     "moe_profile_read": (_i32, [_vp, ctypes.POINTER(MoeProfile)]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_last_hip_error": (_i32, [_vp]),
@@ -217,14 +221,23 @@ def moe_stats(handle: int) -> dict:
     return {"steps": c.steps, "hits": c.hits, "misses": c.misses, "bytes_filled": c.bytes_filled}
 
 
-def moe_profile_enable(handle: int, enable: bool = True) -> None:
-    _check(_lib.moe_profile_enable(handle, int(enable)), "moe_profile_enable", handle)
+def moe_profile_enable(handle: int, mask: int = PROF_ALL, every: int = 1) -> None:
+    """Time one launch in `every` of each kind in `mask` (PROF_* bits; 0 switches timing
+    off)."""
+    _check(_lib.moe_profile_enable(handle, int(mask), int(every)), "moe_profile_enable", handle)
 
 
 def moe_profile_read(handle: int) -> dict:
+    """{kind: {"launches", "ms"}} for route/fill/gate_up/down, plus fill_bytes and
+    ffn_weight_bytes (algorithmic bytes of the FFN since moe_profile_enable)."""
     p = MoeProfile()
     _check(_lib.moe_profile_read(handle, ctypes.byref(p)), "moe_profile_read", handle)
-    return {f: getattr(p, f) for f, _ in MoeProfile._fields_}
+    out = {k: {"launches": int(p.launches[i]), "ms": float(p.ms[i])}
+           for i, k in enumerate(_PROF_KINDS)}
+    out["fill_bytes"] = int(p.fill_bytes)
+    out["ffn_weight_bytes"] = int(p.ffn_weight_bytes)
+    out["gate_up_timed_bytes"] = int(p.gate_up_timed_bytes)
+    return out
 
 
 def moe_status_string(status: int) -> str:

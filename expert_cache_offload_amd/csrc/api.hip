@@ -16,7 +16,8 @@ hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const v
 size_t route_plan_lds_bytes(const Dims& d);
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
-                             int T, int max_entries, int with_combine, hipStream_t s);
+                             int T, int max_entries, int with_combine, int stage,
+                             int count_timed, hipStream_t s);
 int decode_ntok(int T);
 int down_columns_per_block(int fmt);
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
@@ -166,14 +167,16 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Timing of the library's own launches with event pairs from a reusable ring.
 struct Profiler {
-  enum Kind { ROUTE = 0, FILL = 1, FFN = 2, NKIND = 3 };
+  enum Kind { ROUTE = 0, FILL = 1, GATE_UP = 2, DOWN = 3, NKIND = 4 };
   static constexpr int kRing = 4096;
-  bool on = false;
+  int mask = 0;    // bit k: time launches of kind k
+  int every = 1;   // time one launch in `every` of each selected kind
+  int64_t seen[4] = {};
   std::vector<hipEvent_t> a, b;
   std::vector<int> kind;
   size_t head = 0, pending = 0;
-  double ms[NKIND] = {0, 0, 0};
-  int64_t launches[NKIND] = {0, 0, 0};
+  double ms[NKIND] = {};
+  int64_t launches[NKIND] = {};
   unsigned long long stats0[STAT_WORDS] = {};
 
   hipError_t ensure() {
@@ -208,14 +211,15 @@ struct Profiler {
   }
   template <class F>
   hipError_t timed(int k, hipStream_t s, F launch) {
-    if (!on) return launch();
+    if (!(mask >> k & 1)) return launch(false);
+    if (seen[k]++ % every != 0) return launch(false);
     if (pending == (size_t)kRing) {
       hipError_t e = harvest_one();
       if (e != hipSuccess) return e;
     }
     const size_t i = head;
     hipError_t e = hipEventRecord(a[i], s);
-    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess) e = launch(true);
     if (e == hipSuccess) e = hipEventRecord(b[i], s);
     if (e != hipSuccess) return e;
     kind[i] = k;
@@ -227,6 +231,7 @@ struct Profiler {
     for (int k = 0; k < NKIND; ++k) {
       ms[k] = 0;
       launches[k] = 0;
+      seen[k] = 0;
     }
   }
   void destroy() {
@@ -387,7 +392,7 @@ moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t
   if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
   if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = c->prof.timed(Profiler::ROUTE, s, [&] {
+  hipError_t e = c->prof.timed(Profiler::ROUTE, s, [&](bool) {
     return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
   });
   if (e == hipSuccess) e = hipEventRecord(c->ev_plan, s);
@@ -407,7 +412,7 @@ moe_status moe_fill_misses(moe_cache c, int32_t groups, void* fill_stream) {
   // the victim slots.
   hipError_t e = hipStreamWaitEvent(s, c->ev_plan, 0);
   for (int g = 0; g < groups && e == hipSuccess; ++g) {
-    e = c->prof.timed(Profiler::FILL, s, [&] {
+    e = c->prof.timed(Profiler::FILL, s, [&](bool) {
       return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s);
     });
     if (e == hipSuccess) e = hipEventRecord(c->ev_fill[g], s);
@@ -430,21 +435,60 @@ moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
   const int G = c->fill_groups;
   hipError_t e = hipSuccess;
-  if (T > 0)  // hit experts and the shared expert: no fill to wait for
-    e = P.timed(Profiler::FFN, s, [&] {
-      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 0, 0, 1, T,
-                               nu + c->d.has_shared, 0, s);
+  auto both = [&](int sel, int g, int ngroups, int max_entries, int with_combine) {
+    hipError_t r = P.timed(Profiler::GATE_UP, s, [&](bool timed) {
+      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
+                               max_entries, with_combine, 0, timed, s);
     });
+    if (r != hipSuccess) return r;
+    return P.timed(Profiler::DOWN, s, [&](bool timed) {
+      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
+                               max_entries, with_combine, 1, timed, s);
+    });
+  };
+  if (T > 0)  // hit experts and the shared expert: no fill to wait for
+    e = both(0, 0, 1, nu + c->d.has_shared, 0);
   for (int g = 0; g < G && e == hipSuccess; ++g) {
     e = hipStreamWaitEvent(s, c->ev_fill[g], 0);
-    if (e == hipSuccess && T > 0)
-      e = P.timed(Profiler::FFN, s, [&] {
-        return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 1, g, G, T,
-                                 (nu + G - 1) / G, g == G - 1, s);
-      });
+    if (e == hipSuccess && T > 0) e = both(1, g, G, (nu + G - 1) / G, g == G - 1);
   }
   if (e != hipSuccess) return hip_fail(c, e);
   c->state = State::Idle;
+  return MOE_OK;
+}
+
+// The whole step in stream order on one queue: route/plan, the fill of every miss, then
+// one FFN over all the step's experts (hits, shared, misses) and the combine.  No event
+// joins two queues, so consecutive kernels start back to back.
+static moe_status layer_step_serial(moe_cache c, int32_t layer, const void* x, int32_t T,
+                                    const void* w_router, const void* shared_blob,
+                                    int32_t* topk_idx, float* topk_w, void* y, hipStream_t s) {
+  if (T > 0 && (!aligned16(x) || !aligned16(w_router) || ((uintptr_t)y & 3)))
+    return MOE_E_INVALID;
+  if (c->d.has_shared && T > 0 && !aligned16(shared_blob)) return MOE_E_INVALID;
+  auto& P = c->prof;
+  hipError_t e = P.timed(Profiler::ROUTE, s, [&](bool) {
+    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
+  });
+  if (e == hipSuccess)
+    e = P.timed(Profiler::FILL, s, [&](bool) {
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, s);
+    });
+  const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
+  if (e == hipSuccess && T > 0)
+    e = P.timed(Profiler::GATE_UP, s, [&](bool timed) {
+      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 2, 0, 1, T,
+                               nu + c->d.has_shared, 1, 0, timed, s);
+    });
+  if (e == hipSuccess && T > 0)
+    e = P.timed(Profiler::DOWN, s, [&](bool timed) {
+      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 2, 0, 1, T,
+                               nu + c->d.has_shared, 1, 1, timed, s);
+    });
+  if (e != hipSuccess) return hip_fail(c, e);
+  c->plan_T = T;
+  c->plan_layer = layer;
+  c->fill_groups = 1;
   return MOE_OK;
 }
 
@@ -453,12 +497,14 @@ moe_status moe_layer_step(moe_cache c, int32_t layer, const void* x, int32_t T,
                           float* topk_w, void* y, int32_t groups, void* compute_stream,
                           void* fill_stream) {
   if (!c) return MOE_E_INVALID;
-  if (groups <= 0) groups = 2;
-  if (groups > kMaxGroups) return MOE_E_INVALID;
+  if (groups < 0 || groups > kMaxGroups) return MOE_E_INVALID;
   if (c->state != State::Idle) return MOE_E_INVALID;
   if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
   if (T > 0 && (!x || !y || !w_router)) return MOE_E_INVALID;
   if (c->d.has_shared && T > 0 && !shared_blob) return MOE_E_INVALID;
+  if (groups == 0)
+    return layer_step_serial(c, layer, x, T, w_router, shared_blob, topk_idx, topk_w, y,
+                             (hipStream_t)compute_stream);
   moe_status st = moe_route_classify(c, layer, x, T, w_router, topk_idx, topk_w, compute_stream);
   if (st != MOE_OK) return st;
   st = moe_fill_misses(c, groups, fill_stream);
@@ -529,16 +575,18 @@ moe_status moe_stats(moe_cache c, moe_counters* out) {
   return MOE_OK;
 }
 
-moe_status moe_profile_enable(moe_cache c, int32_t enable) {
+moe_status moe_profile_enable(moe_cache c, int32_t mask, int32_t every) {
   if (!c) return MOE_E_INVALID;
   hipError_t e = c->prof.harvest_all();
-  if (e == hipSuccess && enable) e = c->prof.ensure();
+  if (mask < 0 || mask > MOE_PROF_ALL || every < 1) return MOE_E_INVALID;
+  if (e == hipSuccess && mask) e = c->prof.ensure();
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess)
     e = hipMemcpy(c->prof.stats0, c->v.stats, sizeof(c->prof.stats0), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(c, e);
   c->prof.reset();
-  c->prof.on = enable != 0;
+  c->prof.mask = mask;
+  c->prof.every = every;
   return MOE_OK;
 }
 
@@ -550,14 +598,15 @@ moe_status moe_profile_read(moe_cache c, moe_profile* out) {
   if (e == hipSuccess) e = hipMemcpy(st, c->v.stats, sizeof(st), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(c, e);
   const auto& P = c->prof;
-  out->route_launches = P.launches[Profiler::ROUTE];
-  out->fill_launches = P.launches[Profiler::FILL];
-  out->ffn_launches = P.launches[Profiler::FFN];
-  out->route_ms = P.ms[Profiler::ROUTE];
-  out->fill_ms = P.ms[Profiler::FILL];
-  out->ffn_ms = P.ms[Profiler::FFN];
+  for (int k = 0; k < Profiler::NKIND; ++k) {
+    out->launches[k] = P.launches[k];
+    out->ms[k] = P.ms[k];
+  }
   out->fill_bytes = (int64_t)(st[STAT_BYTES] - P.stats0[STAT_BYTES]);
   out->ffn_weight_bytes = (int64_t)(st[STAT_FFN_BYTES] - P.stats0[STAT_FFN_BYTES]);
+  // the gate/up rows and their scales are exactly two thirds of a blob in every format
+  out->gate_up_timed_bytes =
+      (int64_t)((st[STAT_TIMED_BLOB_BYTES] - P.stats0[STAT_TIMED_BLOB_BYTES]) / 3 * 2);
   return MOE_OK;
 }
 

@@ -42,12 +42,13 @@ struct FfnArgs {
   const unsigned char* arena;
   const unsigned char* shared_blob;
   uint16_t* y;  // [T][H] bf16 (combine)
-  int sel;      // 0: hit experts + shared expert, 1: miss group `group` of `ngroups`
+  int sel;      // 0: hit experts + shared expert, 1: miss group `group` of `ngroups`, 2: all
   int group;
   int ngroups;
   int T;
   int NE;  // entry slots of this launch
   int NC;  // combine workgroups (0 unless this is the step's last launch)
+  int timed;  // this launch is bracketed by timing events: count its blob bytes
 };
 
 // ---- format helpers -------------------------------------------------------------
@@ -166,6 +167,10 @@ __device__ __forceinline__ int n_entries_in_launch(const FfnArgs& a, int nHit, i
     first = 0;
     return nHS;
   }
+  if (a.sel == 2) {  // every entry of the step
+    first = 0;
+    return nHS + nMiss;
+  }
   const int m0 = (int)((long long)a.group * nMiss / a.ngroups);
   const int m1 = (int)((long long)(a.group + 1) * nMiss / a.ngroups);
   first = nHS + m0;
@@ -204,8 +209,10 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb, unsigned
   const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntok = en.ntok < NTOK ? en.ntok : NTOK;
-  if (rb == 0 && threadIdx.x == 0)
+  if (rb == 0 && threadIdx.x == 0) {
     atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
+    if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_BLOB_BYTES], (unsigned long long)d.S);
+  }
   // two rows per wave: i0 = r0 + wave, i1 = r0 + wave + 4; their first chunks load before the
   // activations are staged
   const int i0 = rb * RA + wave, i1 = i0 + 4;
@@ -468,16 +475,17 @@ static hipError_t launch_with_lds(Kern kernel, int grid, size_t lds, const FfnAr
   return hipGetLastError();
 }
 
+// stage 0: the gate/up kernel; stage 1: the down kernel (+ combine when a.NC > 0)
 template <int FMT, int NTOK>
-static hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
+static hipError_t launch_ffn(const FfnArgs& a, int stage, hipStream_t s) {
   const Dims& d = a.d;
   constexpr int HC = down_hc<FMT>();
-  hipError_t e = launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA),
-                                 64 + (size_t)NTOK * d.H * 2, a, s);
-  if (e != hipSuccess) return e;
-  e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
-                      sizeof(float) * ((size_t)NTOK * (d.I / d.RS) + (size_t)4 * NTOK * HC), a,
-                      s);
+  if (stage == 0)
+    return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA),
+                           64 + (size_t)NTOK * d.H * 2, a, s);
+  hipError_t e = launch_with_lds(
+      ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
+      sizeof(float) * ((size_t)NTOK * (d.I / d.RS) + (size_t)4 * NTOK * HC), a, s);
   if (e != hipSuccess) return e;
   if (a.NC > 0) {
     hipLaunchKernelGGL(combine_kernel, dim3(a.NC), dim3(FT), 0, s, a);
@@ -487,12 +495,12 @@ static hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
 }
 
 template <int FMT>
-static hipError_t launch_fmt(const FfnArgs& a, int ntok, hipStream_t s) {
+static hipError_t launch_fmt(const FfnArgs& a, int ntok, int stage, hipStream_t s) {
   switch (ntok) {
-    case 1: return launch_ffn<FMT, 1>(a, s);
-    case 2: return launch_ffn<FMT, 2>(a, s);
-    case 4: return launch_ffn<FMT, 4>(a, s);
-    default: return launch_ffn<FMT, 8>(a, s);
+    case 1: return launch_ffn<FMT, 1>(a, stage, s);
+    case 2: return launch_ffn<FMT, 2>(a, stage, s);
+    case 4: return launch_ffn<FMT, 4>(a, stage, s);
+    default: return launch_ffn<FMT, 8>(a, stage, s);
   }
 }
 
@@ -501,21 +509,24 @@ int down_columns_per_block(int fmt) {
                          : fmt == FMT_FP8 ? down_hc<FMT_FP8>() : down_hc<FMT_MXFP4>();
 }
 
-// sel 0: hit experts and the shared expert; sel 1: miss group `group` of `ngroups`.
+// sel 0: hit experts and the shared expert; sel 1: miss group `group` of `ngroups`;
+// sel 2: every entry of the step (hits, shared, misses).
 // max_entries bounds the entries of the launch; with_combine adds the combine kernel after
-// it (only on the step's last launch).
+// the down kernel (only on the step's last launch); stage 0 launches the gate/up kernel,
+// stage 1 the down kernel (and the combine).
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
-                             int T, int max_entries, int with_combine, hipStream_t s) {
+                             int T, int max_entries, int with_combine, int stage,
+                             int count_timed, hipStream_t s) {
   const int nc = with_combine ? T * ((d.H + FT - 1) / FT) : 0;
   FfnArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
             (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
-            max_entries > 0 ? max_entries : 0, nc};
+            max_entries > 0 ? max_entries : 0, nc, count_timed};
   const int ntok = decode_ntok(T);
   switch (d.fmt) {
-    case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, s);
-    case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, s);
-    default: return launch_fmt<FMT_MXFP4>(a, ntok, s);
+    case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, stage, s);
+    case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, stage, s);
+    default: return launch_fmt<FMT_MXFP4>(a, ntok, stage, s);
   }
 }
 

@@ -42,6 +42,7 @@ enum : int {
   STAT_MISSES = 2,
   STAT_BYTES = 3,
   STAT_FFN_BYTES = 4,
+  STAT_TIMED_BLOB_BYTES = 5,  // blobs read by gate/up launches bracketed by timing events
   STAT_WORDS = 8
 };
 

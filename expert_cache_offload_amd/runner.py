@@ -97,7 +97,7 @@ class Workbench:
         moe_route_classify(self.handle, l, self.x_ptr(t, l), self.T, self.router[l].data_ptr(),
                            self.topk_idx[l].data_ptr(), self.topk_w[l].data_ptr(),
                            self.compute.cuda_stream)
-        moe_fill_misses(self.handle, self.groups, self.fill.cuda_stream)
+        moe_fill_misses(self.handle, max(1, self.groups), self.fill.cuda_stream)
         moe_expert_ffn(self.handle, l, self.x_ptr(t, l), self.T, self.shared_ptr(l),
                        self.y[l].data_ptr(), self.compute.cuda_stream)
 

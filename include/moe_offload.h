@@ -168,8 +168,11 @@ moe_status moe_fill_misses(moe_cache cache, int32_t groups, void* fill_stream);
 moe_status moe_expert_ffn(moe_cache cache, int32_t layer, const void* x, int32_t T,
                           const void* shared_blob, void* y, void* stream);
 
-/* One whole layer step: moe_route_classify + moe_fill_misses(groups) +
- * moe_expert_ffn.  groups <= 0 picks 2. */
+/* One whole layer step.  groups >= 1: moe_route_classify + moe_fill_misses(groups) on
+ * fill_stream + moe_expert_ffn, hit experts computing while the misses transfer.
+ * groups == 0: the same step in stream order on compute_stream alone (route/plan, fill of
+ * every miss, one FFN over all the step's experts, combine); fill_stream is ignored.
+ * Both give identical results. */
 moe_status moe_layer_step(moe_cache cache, int32_t layer, const void* x, int32_t T,
                           const void* w_router, const void* shared_blob, int32_t* topk_idx,
                           float* topk_w, void* y, int32_t groups, void* compute_stream,
@@ -188,19 +191,28 @@ moe_status moe_plan_read(moe_cache cache, moe_plan_host* out);
 /* Synchronous read of the device-side counters. */
 moe_status moe_stats(moe_cache cache, moe_counters* out);
 
-/* Per-kernel timing of the library's own launches, for measurement.  When enabled,
- * every route, fill and FFN launch is bracketed by a pair of timing events on the
- * stream it runs on (eager calls only: do not enable while a stream is captured).
- * moe_profile_enable resets the accumulators; moe_profile_read synchronises.
- * ffn_weight_bytes counts the expert-weight bytes the FFN kernels were given
- * (each processed expert blob once), i.e. the algorithmic bytes of the FFN. */
+/* Per-kernel timing of the library's own launches, for measurement.  One launch in every
+ * `every` (>= 1) of each kind selected in `mask` is bracketed by a pair of timing events on
+ * the stream it runs on (eager calls only: do not enable while a stream is captured).  A
+ * timing event costs queue time, so sampling keeps the timed run close to an untimed one.  Kinds: route/plan kernel,
+ * fill kernel, FFN gate/up kernel, FFN down kernel (with the combine when it follows).
+ * moe_profile_enable resets the accumulators (mask 0 switches timing off); moe_profile_read
+ * synchronises.  ffn_weight_bytes counts the expert-weight bytes the FFN kernels were given
+ * (each processed expert blob once): the algorithmic bytes of the FFN, of which the gate/up
+ * kernel reads exactly two thirds in every weight format. */
+#define MOE_PROF_ROUTE 1
+#define MOE_PROF_FILL 2
+#define MOE_PROF_GATE_UP 4
+#define MOE_PROF_DOWN 8
+#define MOE_PROF_ALL 15
 typedef struct {
-  int64_t route_launches, fill_launches, ffn_launches;
-  double route_ms, fill_ms, ffn_ms;
+  int64_t launches[4]; /* route, fill, gate/up, down */
+  double ms[4];        /* summed event-pair durations, same order */
   int64_t fill_bytes, ffn_weight_bytes;
+  int64_t gate_up_timed_bytes; /* algorithmic bytes of the timed gate/up launches */
 } moe_profile;
 
-moe_status moe_profile_enable(moe_cache cache, int32_t enable);
+moe_status moe_profile_enable(moe_cache cache, int32_t mask, int32_t every);
 moe_status moe_profile_read(moe_cache cache, moe_profile* out);
 
 const char* moe_status_string(moe_status s);

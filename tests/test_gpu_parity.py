@@ -72,13 +72,19 @@ def test_tiny_decode_every_step_and_slot_bytes():
     _log(f"tiny: max rel-L2 {max(errs):.2e}, misses {st['misses']}")
 
 
+def test_tiny_single_queue_mode():
+    wl = mi.WORKLOADS["tiny"].with_steps(24)
+    with _bench(wl, groups=0) as wb:
+        run_parity(wb, 24, slot_bytes=True)
+
+
 def test_tiny_through_separate_calls():
     wl = mi.WORKLOADS["tiny"].with_steps(24)
     with _bench(wl, groups=3) as wb:
         run_parity(wb, 24, parts=True)
 
 
-@pytest.mark.parametrize("groups", [1, 2, 8])
+@pytest.mark.parametrize("groups", [0, 1, 2, 8])
 def test_bf16_decode_multilayer_evictions(groups):
     """35B-A3B expert shape (H 2048, 128 experts top-8, I 768) with 4 layers sharing a 30% cache."""
     wl = mi.WORKLOADS["qwen35b_decode"].with_layers(4).with_steps(24)
@@ -88,22 +94,24 @@ def test_bf16_decode_multilayer_evictions(groups):
     _log(f"bf16 4-layer: max rel-L2 {max(errs):.2e}")
 
 
-def test_fp8_decode_with_shared_expert():
+@pytest.mark.parametrize("groups", [0, 2])
+def test_fp8_decode_with_shared_expert(groups):
     """284B-like shape: H 4096, 256 experts top-8 + shared expert, fp8 e4m3 1x128 blocks."""
     wl = mi.WORKLOADS["dsv4_fp8_decode"].with_layers(2).with_steps(12)
-    _log(f"case {wl.name} C={wl.capacity}")
-    with _bench(wl) as wb:
+    _log(f"case {wl.name} groups={groups} C={wl.capacity}")
+    with _bench(wl, groups=groups) as wb:
         errs = run_parity(wb, wl.token_steps, ffn_every=5)
     _log(f"fp8: max rel-L2 {max(errs):.2e}")
 
 
-def test_mxfp4_four_streams_with_resize():
+@pytest.mark.parametrize("groups", [0, 2])
+def test_mxfp4_four_streams_with_resize(groups):
     """753B-like shape: H 6144, 256 experts top-8, MXFP4, 4 streams per step with cross-request
     dedup; the cache shrinks from 40% to 15% of the pool at a safe point."""
     wl = dataclasses.replace(mi.WORKLOADS["glm_mxfp4_4stream"].with_layers(2), token_steps=16,
                              resize_at=8)
-    _log(f"case {wl.name} C={wl.capacity}->{wl.resize_capacity}")
-    with _bench(wl) as wb:
+    _log(f"case {wl.name} groups={groups} C={wl.capacity}->{wl.resize_capacity}")
+    with _bench(wl, groups=groups) as wb:
         errs = run_parity(wb, wl.token_steps, ffn_every=6)
     _log(f"mxfp4: max rel-L2 {max(errs):.2e}")
 
