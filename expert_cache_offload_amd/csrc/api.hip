@@ -20,6 +20,7 @@ hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const v
                              int count_timed, hipStream_t s);
 int decode_ntok(int T);
 int down_columns_per_block(int fmt);
+int down_row_splits(int inter);
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
                        int ngroups, int grid, hipStream_t s);
 hipError_t launch_init(const Dev& v, int max_capacity, int n_keys, int capacity, hipStream_t s);
@@ -33,7 +34,7 @@ using namespace moe;
 namespace {
 
 constexpr int kMaxGroups = kMaxFillGroups;
-constexpr int kMaxCapacity = 4096;  // LDS-resident LRU stamps and the resize sort
+constexpr int kMaxCapacity = kMaxSlots;  // LDS-resident LRU stamps and the resize sort
 // Fill workgroups: 32 saturate the PCIe link (57 GB/s measured) while leaving HBM streaming
 // of concurrent kernels untouched; 256 workgroups collapse a concurrent HBM stream to <2%.
 constexpr int kFillGrid = 32;
@@ -62,9 +63,7 @@ Dims make_dims(const moe_shape& s, int max_capacity) {
   d.amax = s.max_tokens * s.top_k;
   d.umax = d.amax < s.experts ? d.amax : s.experts;
   d.max_capacity = max_capacity;
-  // Split the down projection's rows in two when one launch would not fill the chip.
-  const int col_blocks = s.hidden / down_columns_per_block(s.wfmt);
-  d.RS = (d.umax * col_blocks < 512) ? 2 : 1;
+  d.RS = down_row_splits(s.inter);
   d.S = s.blob_bytes;
   return d;
 }

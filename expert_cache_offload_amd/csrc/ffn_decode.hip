@@ -41,13 +41,13 @@ struct FfnArgs {
   const uint16_t* x;  // [T][H] bf16
   const unsigned char* arena;
   const unsigned char* shared_blob;
-  uint16_t* y;  // [T][H] bf16 (combine)
+  uint16_t* y;  // [T][H] bf16, written by the combine
   int sel;      // 0: hit experts + shared expert, 1: miss group `group` of `ngroups`, 2: all
   int group;
   int ngroups;
   int T;
   int NE;  // entry slots of this launch
-  int NC;  // combine workgroups (0 unless this is the step's last launch)
+  int NC;     // combine workgroups (0 unless this is the step's last launch)
   int timed;  // this launch is bracketed by timing events: count its blob bytes
 };
 
@@ -201,8 +201,13 @@ __device__ __forceinline__ bool resolve(const FfnArgs& a, int j, Entry& en) {
 }
 
 // ---------------------------------------------------------------- gate / up role
+// No LDS and no barrier: every wave owns two rows, puts all of its weight loads in flight
+// first (the chain hdr -> entry -> slot is the only dependency), then reads the token
+// activations (a few KiB, shared by all waves through the L1) and reduces across the wave.
+constexpr int GPF = 8;  // 16-byte chunks per lane per row kept in flight
+
 template <int FMT, int NTOK>
-__device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb, unsigned char* smem) {
+__device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb) {
   using F = Fmt<FMT>;
   constexpr int EPL = F::EPL;
   const Dims& d = a.d;
@@ -213,67 +218,77 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb, unsigned
     atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
     if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_BLOB_BYTES], (unsigned long long)d.S);
   }
-  // two rows per wave: i0 = r0 + wave, i1 = r0 + wave + 4; their first chunks load before the
-  // activations are staged
   const int i0 = rb * RA + wave, i1 = i0 + 4;
   const size_t rbytes = F::row_bytes(2 * H);
   const uint4* row0 = (const uint4*)(en.blob + (size_t)i0 * rbytes);
   const uint4* row1 = (const uint4*)(en.blob + (size_t)i1 * rbytes);
-  const int nq = 2 * H / EPL;
-  int* s_tok = (int*)smem;              // [NTOK]
-  float* s_w = (float*)(s_tok + NTOK);  // [NTOK]
-  uint16_t* xs = (uint16_t*)(smem + 64);  // [NTOK][H]
-  if ((int)threadIdx.x < ntok) {
-    const int q = threadIdx.x;
-    s_tok[q] = en.shared ? q : a.v.row_tok[en.row0 + q];
-    s_w[q] = en.shared ? 1.0f : a.v.row_w[en.row0 + q];
+  const int nq = 2 * H / EPL;          // 16-byte chunks per row
+  const int nper = (nq + 63) / 64;     // per lane
+  int tok[NTOK];
+  float wt[NTOK];
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    tok[t] = 0;
+    wt[t] = 0.f;
   }
-  __syncthreads();
-  for (int q = 0; q < ntok; ++q) {
-    const uint4* src = (const uint4*)(a.x + (size_t)s_tok[q] * H);
-    uint4* dst = (uint4*)(xs + (size_t)q * H);
-    for (int c = threadIdx.x; c < H / 8; c += FT) dst[c] = src[c];
-  }
-  __syncthreads();
   float g0[NTOK], u0[NTOK], g1[NTOK], u1[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) g0[t] = u0[t] = g1[t] = u1[t] = 0.f;
-#pragma unroll 4
-  for (int q = lane; q < nq; q += 64) {
-    const uint4 w0 = row0[q];
-    const uint4 w1 = row1[q];
-    const int p = q * EPL;
-    const bool isg = p < H;
-    const int xp = isg ? p : p - H;
-    float f0[EPL], f1[EPL];
-    F::unpack(w0, f0);
-    F::unpack(w1, f1);
-    const float s0 = gu_scale<FMT>(en.blob, H, I, i0, isg ? 0 : 1, xp);
-    const float s1 = gu_scale<FMT>(en.blob, H, I, i1, isg ? 0 : 1, xp);
+  for (int base = 0; base < nper; base += GPF) {
+    uint4 w0[GPF], w1[GPF];
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t) {
-      if (t < ntok) {
-        const uint4* xv = (const uint4*)(xs + (size_t)t * H + xp);
-        float d0 = 0.f, d1 = 0.f;
+    for (int k = 0; k < GPF; ++k) {
+      if ((base + k) * 64 + lane < nq) {
+        w0[k] = row0[(base + k) * 64 + lane];
+        w1[k] = row1[(base + k) * 64 + lane];
+      }
+    }
+    if (base == 0) {
 #pragma unroll
-        for (int c8 = 0; c8 < EPL / 8; ++c8) {
-          const uint4 xx = xv[c8];
-          const float xf[8] = {bf16_lo(xx.x), bf16_hi(xx.x), bf16_lo(xx.y), bf16_hi(xx.y),
-                               bf16_lo(xx.z), bf16_hi(xx.z), bf16_lo(xx.w), bf16_hi(xx.w)};
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            d0 += f0[c8 * 8 + c] * xf[c];
-            d1 += f1[c8 * 8 + c] * xf[c];
-          }
+      for (int t = 0; t < NTOK; ++t) {
+        if (t < ntok) {
+          tok[t] = en.shared ? t : a.v.row_tok[en.row0 + t];
+          wt[t] = en.shared ? 1.0f : a.v.row_w[en.row0 + t];
         }
-        d0 *= s0;
-        d1 *= s1;
-        if (isg) {
-          g0[t] += d0;
-          g1[t] += d1;
-        } else {
-          u0[t] += d0;
-          u1[t] += d1;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < GPF; ++k) {
+      if ((base + k) * 64 + lane < nq) {
+        const int p = ((base + k) * 64 + lane) * EPL;
+        const bool isg = p < H;
+        const int xp = isg ? p : p - H;
+        float f0[EPL], f1[EPL];
+        F::unpack(w0[k], f0);
+        F::unpack(w1[k], f1);
+        const float s0 = gu_scale<FMT>(en.blob, H, I, i0, isg ? 0 : 1, xp);
+        const float s1 = gu_scale<FMT>(en.blob, H, I, i1, isg ? 0 : 1, xp);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+          if (t < ntok) {
+            const uint4* xv = (const uint4*)(a.x + (size_t)tok[t] * H + xp);
+            float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+            for (int c8 = 0; c8 < EPL / 8; ++c8) {
+              const uint4 xx = xv[c8];
+              const float xf[8] = {bf16_lo(xx.x), bf16_hi(xx.x), bf16_lo(xx.y), bf16_hi(xx.y),
+                                   bf16_lo(xx.z), bf16_hi(xx.z), bf16_lo(xx.w), bf16_hi(xx.w)};
+#pragma unroll
+              for (int c = 0; c < 8; ++c) {
+                d0 += f0[c8 * 8 + c] * xf[c];
+                d1 += f1[c8 * 8 + c] * xf[c];
+              }
+            }
+            d0 *= s0;
+            d1 *= s1;
+            if (isg) {
+              g0[t] += d0;
+              g1[t] += d1;
+            } else {
+              u0[t] += d0;
+              u1[t] += d1;
+            }
+          }
         }
       }
     }
@@ -291,110 +306,117 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb, unsigned
       }
       if (lane == 0) {
         float* out = act + (size_t)(en.row0 + t) * I;
-        out[i0] = silu(a0) * b0 * s_w[t];
-        out[i1] = silu(a1) * b1 * s_w[t];
+        out[i0] = silu(a0) * b0 * wt[t];
+        out[i1] = silu(a1) * b1 * wt[t];
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- down role
+// A workgroup owns a column block of DTC*DC columns of the stored transpose WdT and I/RS of
+// its rows; thread (row lane rl, column lane cl) owns DC columns of a contiguous run of at
+// most DMAXR rows.  All of a thread's weight loads go out first; the activations (fp32,
+// L1-shared) follow, then row lanes reduce by shuffles and through LDS across waves.  The
+// workgroup writes one partial sum per row split; the combine adds the splits.
+constexpr int DTC = 16;            // column lanes
+constexpr int DTR = FT / DTC;      // row lanes
+constexpr int DMAXR = 16;          // rows per thread, at most
+
+template <int FMT>
+struct DVec {
+  using T = uint4;
+};
+template <>
+struct DVec<FMT_MXFP4> {
+  using T = uint2;
+};
+
+template <int FMT>
+__device__ __forceinline__ void unpack_d(const typename DVec<FMT>::T& w, float* f);
+template <>
+__device__ __forceinline__ void unpack_d<FMT_BF16>(const uint4& w, float* f) {
+  Fmt<FMT_BF16>::unpack(w, f);
+}
+template <>
+__device__ __forceinline__ void unpack_d<FMT_FP8>(const uint4& w, float* f) {
+  Fmt<FMT_FP8>::unpack(w, f);
+}
+template <>
+__device__ __forceinline__ void unpack_d<FMT_MXFP4>(const uint2& w, float* f) {
+  fp4x8(w.x, f);
+  fp4x8(w.y, f + 8);
+}
+
 template <int FMT, int NTOK>
 __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, unsigned char* smem) {
   using F = Fmt<FMT>;
+  using W = typename DVec<FMT>::T;
   constexpr int DC = F::DC;
-  constexpr int HC = 8 * DC;  // columns per workgroup: 8 threads per row segment
+  constexpr int HC = DTC * DC;
   const Dims& d = a.d;
   const int H = d.H, I = d.I, RS = d.RS;
   const int ntok = en.ntok < NTOK ? en.ntok : NTOK;
-  const int IR = I / RS;  // rows of this split
-  const int i_begin = rs * IR;
-  float* s_a = (float*)smem;               // [NTOK][IR]
-  float* s_red = s_a + (size_t)NTOK * IR;  // [4][NTOK][HC]
+  const int IR = I / RS;
+  const int nrw = IR / DTR;  // <= DMAXR (host-chosen RS)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cg = threadIdx.x & 7, rl = threadIdx.x >> 3;  // column group, row lane (0..31)
-  const int c0 = cb * HC + cg * DC;
-  const int nrw = IR / 32;  // contiguous rows per thread
-  const int ra = i_begin + rl * nrw;
+  const int cl = threadIdx.x % DTC, rl = threadIdx.x / DTC;
+  const int c0 = cb * HC + cl * DC;
+  const int ra = rs * IR + rl * nrw;
   const unsigned char* wdt = en.blob + F::row_bytes(2 * H) * (size_t)I;  // WdT after Wgu
   const size_t drow = F::row_bytes(H);
-  const size_t cbyte = F::row_bytes(c0);
-  const float* act = en.shared ? a.v.act_shared : a.v.act;
-  for (int q = 0; q < ntok; ++q)
-    for (int i = threadIdx.x; i < IR; i += FT)
-      s_a[q * IR + i] = act[(size_t)(en.row0 + q) * I + i_begin + i];
-  __syncthreads();
+  const unsigned char* wp = wdt + (size_t)ra * drow + F::row_bytes(c0);
+  W w[DMAXR];
+#pragma unroll
+  for (int r = 0; r < DMAXR; ++r)
+    if (r < nrw) w[r] = *(const W*)(wp + (size_t)r * drow);
+  float sc0[DC], sc1[DC];
+  int bsplit = DMAXR;  // first r that uses sc1
+  if constexpr (F::SB > 0) {
+    const int blk0 = ra / F::SB, blk1 = (ra + nrw - 1) / F::SB;
+    d_scales<FMT>(en.blob, H, I, blk0, c0, sc0);
+    d_scales<FMT>(en.blob, H, I, blk1, c0, sc1);
+    bsplit = (blk0 + 1) * F::SB - ra;
+  }
+  const float* act = (en.shared ? a.v.act_shared : a.v.act) + (size_t)en.row0 * I + ra;
   float acc[NTOK][DC];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t)
 #pragma unroll
     for (int c = 0; c < DC; ++c) acc[t][c] = 0.f;
-
-  if constexpr (F::SB == 0) {
-#pragma unroll 8
-    for (int r = 0; r < nrw; ++r) {
-      const int i = ra + r;
+#pragma unroll
+  for (int r = 0; r < DMAXR; ++r) {
+    if (r < nrw) {
       float f[DC];
-      F::load_d(wdt + (size_t)i * drow + cbyte, f);
+      unpack_d<FMT>(w[r], f);
+      if constexpr (F::SB > 0) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) f[c] *= (r < bsplit ? sc0[c] : sc1[c]);
+      }
 #pragma unroll
       for (int t = 0; t < NTOK; ++t) {
         if (t < ntok) {
-          const float at = s_a[t * IR + (i - i_begin)];
+          const float at = act[(size_t)t * I + r];
 #pragma unroll
           for (int c = 0; c < DC; ++c) acc[t][c] += at * f[c];
         }
       }
     }
-  } else {
-    // rows of one scale block accumulate unscaled, then the block's column scales apply once
-    int r = 0;
-    while (r < nrw) {
-      const int i = ra + r;
-      const int blk = i / F::SB;
-      const int rend_blk = (blk + 1) * F::SB - ra;  // first r past this block
-      const int r1 = rend_blk < nrw ? rend_blk : nrw;
-      float bacc[NTOK][DC];
-#pragma unroll
-      for (int t = 0; t < NTOK; ++t)
-#pragma unroll
-        for (int c = 0; c < DC; ++c) bacc[t][c] = 0.f;
-#pragma unroll 4
-      for (; r < r1; ++r) {
-        const int ii = ra + r;
-        float f[DC];
-        F::load_d(wdt + (size_t)ii * drow + cbyte, f);
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) {
-          if (t < ntok) {
-            const float at = s_a[t * IR + (ii - i_begin)];
-#pragma unroll
-            for (int c = 0; c < DC; ++c) bacc[t][c] += at * f[c];
-          }
-        }
-      }
-      float sc[DC];
-      d_scales<FMT>(en.blob, H, I, blk, c0, sc);
-#pragma unroll
-      for (int t = 0; t < NTOK; ++t)
-#pragma unroll
-        for (int c = 0; c < DC; ++c) acc[t][c] += bacc[t][c] * sc[c];
-    }
   }
-  // reduce over the 32 row lanes sharing a column group: 8 per wave by shuffles, 4 waves in LDS
+  // reduce over the DTR row lanes: those inside a wave by shuffles, the 4 waves through LDS
+  float* s_red = (float*)smem;  // [4][NTOK][HC]
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
     if (t < ntok) {
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        float s = acc[t][c];
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        acc[t][c] = s;
+        float v = acc[t][c];
+        for (int off = DTC; off < 64; off <<= 1) v += __shfl_xor(v, off);
+        acc[t][c] = v;
       }
     }
   }
-  if (lane < 8) {
+  if (lane < DTC) {
 #pragma unroll
     for (int t = 0; t < NTOK; ++t)
       if (t < ntok)
@@ -406,15 +428,16 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
   float* yexp = en.shared ? a.v.yexp_shared : a.v.yexp;
   for (int idx = threadIdx.x; idx < ntok * HC; idx += FT) {
     const int t = idx / HC, c = idx % HC;
-    float s = 0.f;
+    float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < FT / 64; ++w) s += s_red[((size_t)w * NTOK + t) * HC + c];
-    yexp[((size_t)(en.row0 + t) * RS + rs) * H + cb * HC + c] = s;
+    for (int wv = 0; wv < FT / 64; ++wv) sum += s_red[((size_t)wv * NTOK + t) * HC + c];
+    yexp[((size_t)(en.row0 + t) * RS + rs) * H + cb * HC + c] = sum;
   }
 }
 
 // ---------------------------------------------------------------- combine role
-// y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + sum_rs yexp_shared[t][rs] ), fixed order.
+// y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + sum_rs yexp_shared[t][rs] ), in that fixed
+// order.
 __device__ void combine_role(const FfnArgs& a, int cblk) {
   const Dims& d = a.d;
   const Dev& v = a.v;
@@ -425,26 +448,38 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
   if ((int)threadIdx.x < d.K) s_pos[threadIdx.x] = v.inv_pos[t * d.K + threadIdx.x];
   __syncthreads();
   if (c >= d.H) return;
+  // all partials of a chunk are loaded before any is added: one memory latency per chunk
+  constexpr int CH = 16;
+  const int RS = d.RS, nrouted = d.K * RS, nall = nrouted + (d.has_shared ? RS : 0);
   float s = 0.f;
-  for (int jj = 0; jj < d.K; ++jj)
-    for (int rs = 0; rs < d.RS; ++rs) s += v.yexp[((size_t)s_pos[jj] * d.RS + rs) * d.H + c];
-  if (d.has_shared)
-    for (int rs = 0; rs < d.RS; ++rs) s += v.yexp_shared[((size_t)t * d.RS + rs) * d.H + c];
+  for (int base = 0; base < nall; base += CH) {
+    float pv[CH];
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int i = base + q;
+      pv[q] = 0.f;
+      if (i < nrouted)
+        pv[q] = v.yexp[((size_t)s_pos[i / RS] * RS + i % RS) * d.H + c];
+      else if (i < nall)
+        pv[q] = v.yexp_shared[((size_t)t * RS + (i - nrouted)) * d.H + c];
+    }
+#pragma unroll
+    for (int q = 0; q < CH; ++q) s += pv[q];
+  }
   a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
 }
 
 template <int FMT>
 static constexpr int down_hc() {
-  return 8 * Fmt<FMT>::DC;
+  return DTC * Fmt<FMT>::DC;
 }
 
 template <int FMT, int NTOK>
 __global__ __launch_bounds__(FT) void ffn_gate_up_kernel(FfnArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
   const int nra = a.d.I / RA;
   Entry en;
   if (!resolve(a, blockIdx.x / nra, en)) return;
-  gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra, smem);
+  gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra);
 }
 
 template <int FMT, int NTOK>
@@ -480,12 +515,9 @@ template <int FMT, int NTOK>
 static hipError_t launch_ffn(const FfnArgs& a, int stage, hipStream_t s) {
   const Dims& d = a.d;
   constexpr int HC = down_hc<FMT>();
-  if (stage == 0)
-    return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA),
-                           64 + (size_t)NTOK * d.H * 2, a, s);
-  hipError_t e = launch_with_lds(
-      ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
-      sizeof(float) * ((size_t)NTOK * (d.I / d.RS) + (size_t)4 * NTOK * HC), a, s);
+  if (stage == 0) return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA), 0, a, s);
+  hipError_t e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
+                                 sizeof(float) * (size_t)4 * NTOK * HC, a, s);
   if (e != hipSuccess) return e;
   if (a.NC > 0) {
     hipLaunchKernelGGL(combine_kernel, dim3(a.NC), dim3(FT), 0, s, a);
@@ -509,11 +541,19 @@ int down_columns_per_block(int fmt) {
                          : fmt == FMT_FP8 ? down_hc<FMT_FP8>() : down_hc<FMT_MXFP4>();
 }
 
+// Row splits of the down projection: the fewest (a power of two) that keep a thread's rows
+// within DMAXR.  I is a multiple of 128, so I / (RS * DTR) is whole for every RS it picks.
+int down_row_splits(int inter) {
+  int rs = 1;
+  while (inter / (rs * DTR) > DMAXR) rs *= 2;
+  return rs;
+}
+
 // sel 0: hit experts and the shared expert; sel 1: miss group `group` of `ngroups`;
-// sel 2: every entry of the step (hits, shared, misses).
-// max_entries bounds the entries of the launch; with_combine adds the combine kernel after
-// the down kernel (only on the step's last launch); stage 0 launches the gate/up kernel,
-// stage 1 the down kernel (and the combine).
+// sel 2: every entry of the step (hits, shared, misses).  max_entries bounds the entries of
+// the launch; with_combine adds the combine kernel after the down kernel (only on the step's
+// last launch); stage 0 launches the gate/up kernel, stage 1 the down kernel (and the
+// combine).
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
                              int T, int max_entries, int with_combine, int stage,

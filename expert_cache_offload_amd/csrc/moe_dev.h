@@ -36,6 +36,7 @@ enum : int {
   HDR_WORDS = 16
 };
 enum : int { ERR_CAPACITY = 1 };
+constexpr int kMaxSlots = 4096;  // most cache slots a handle supports (LDS-resident LRU)
 enum : int {
   STAT_STEPS = 0,
   STAT_HITS = 1,

@@ -17,7 +17,8 @@
 //   distinct experts U already ascending;
 //   hit/miss classification against slot_of;
 //   LRU victims as the `need` smallest (stamp, key) among occupied slots not in U, found
-//   in rounds of "oldest remaining stamp" from LDS-resident stamps;
+//   in rounds of "oldest remaining stamp" over the LDS-resident stamps (one round per
+//   distinct stamp taken: a step stamps all its experts alike);
 //   slot-table update and the per-expert token lists consumed by the FFN.
 // The rule reproduced (free slots [n, C) first in ascending order, then victims in
 // (stamp, key) order; misses taken in ascending expert id; all of U stamped with the
@@ -27,6 +28,7 @@
 namespace moe {
 
 constexpr int RT = 256;  // threads per route workgroup (4 waves)
+constexpr int kSlotsPerThread = kMaxSlots / RT;
 
 struct RouteArgs {
   Dims d;
@@ -88,20 +90,40 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = 0.0;
     const uint16_t* wrow = a.wr + (size_t)e * H;
-    for (int h = lane * 8; h < H; h += 64 * 8) {
-      uint4 w = *(const uint4*)(wrow + h);
-      float wf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                     bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    // chunks of 8 elements per lane, RCH chunks' loads (weights and activations) in flight
+    // before any arithmetic
+    constexpr int RCH = 4;
+    const int nch = (H + 511) / 512;  // H is a multiple of 256: the last chunk may be half
+    for (int base = 0; base < nch; base += RCH) {
+      uint4 w[RCH], xv[RCH][kDecodeMaxTokens];
 #pragma unroll
-      for (int t = 0; t < kDecodeMaxTokens; ++t) {
-        if (t < T) {
-          uint4 xv = *(const uint4*)(a.x + (size_t)t * H + h);
-          float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                         bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-          double s = 0.0;
+      for (int k = 0; k < RCH; ++k) {
+        const int h = (base + k) * 512 + lane * 8;
+        if (base + k < nch && h < H) {
+          w[k] = *(const uint4*)(wrow + h);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) s += (double)(wf[c] * xf[c]);  // product exact in fp32
-          acc[t] += s;
+          for (int t = 0; t < kDecodeMaxTokens; ++t)
+            if (t < T) xv[k][t] = *(const uint4*)(a.x + (size_t)t * H + h);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RCH; ++k) {
+        if (base + k < nch && (base + k) * 512 + lane * 8 < H) {
+          const float wf[8] = {bf16_lo(w[k].x), bf16_hi(w[k].x), bf16_lo(w[k].y),
+                               bf16_hi(w[k].y), bf16_lo(w[k].z), bf16_hi(w[k].z),
+                               bf16_lo(w[k].w), bf16_hi(w[k].w)};
+#pragma unroll
+          for (int t = 0; t < kDecodeMaxTokens; ++t) {
+            if (t < T) {
+              const uint4 q = xv[k][t];
+              const float xf[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
+                                   bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w)};
+              double s = 0.0;
+#pragma unroll
+              for (int c = 0; c < 8; ++c) s += (double)(wf[c] * xf[c]);  // exact fp32 product
+              acc[t] += s;
+            }
+          }
         }
       }
     }
@@ -133,12 +155,14 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   // ---------------- phase B (one workgroup) ----------------
   const int A = T * K;
   const int umax = d.umax;
+  const int layer = a.layer;
   // LDS carve-up
   unsigned char* p = smem;
   uint64_t* s_comp = (uint64_t*)p;  p += sizeof(uint64_t) * d.max_capacity;
   double* s_z = (double*)p;         p += sizeof(double) * (size_t)d.max_tokens * E;
   int* s_cnt = (int*)p;             p += sizeof(int) * E;
   int* s_uidx = (int*)p;            p += sizeof(int) * E;
+  int* s_srow = (int*)p;            p += sizeof(int) * E;
   int* s_tk_idx = (int*)p;          p += sizeof(int) * d.amax;
   float* s_tk_w = (float*)p;        p += sizeof(float) * d.amax;
   double* s_tk_z = (double*)p;      p += sizeof(double) * d.amax;
@@ -148,6 +172,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   int* s_hit = (int*)p;             p += sizeof(int) * umax;
   int* s_miss = (int*)p;            p += sizeof(int) * umax;
   int* s_vict = (int*)p;            p += sizeof(int) * umax;
+  int* s_vkey = (int*)p;            p += sizeof(int) * umax;
   int* s_grp = (int*)p;             p += sizeof(int) * umax;
   int* s_sorted = (int*)p;          p += sizeof(int) * umax;
   int* s_aslot = (int*)p;           p += sizeof(int) * umax;
@@ -157,19 +182,37 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   __shared__ uint64_t s_tmp64[8];
   __shared__ int s_g;
 
+  // Every global read of the plan goes out together: the logits, this layer's row of
+  // slot_of and the control words; the occupied slots' (stamp, key) follow as soon as the
+  // occupancy is known and stay in registers until the victim search.
+  for (int i = threadIdx.x; i < T * E; i += RT) {
+    const double z = v.logits[i];
+    s_z[i] = (z == z) ? z : -__builtin_huge_val();  // NaN ranks as -inf
+  }
   for (int e = threadIdx.x; e < E; e += RT) {
     s_cnt[e] = 0;
     s_uidx[e] = -1;
+    s_srow[e] = v.slot_of[layer * E + e];
   }
-
-  // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
-  // the experts of rank < K are the selection, in order.  NaN logits count as -inf so the
-  // ranks stay a permutation.
-  for (int i = threadIdx.x; i < T * E; i += RT) {
-    const double z = v.logits[i];
-    s_z[i] = (z == z) ? z : -__builtin_huge_val();
+  const int n = v.ctrl[CTRL_N];
+  const int C = v.ctrl[CTRL_C];
+  const long long step = (long long)(unsigned)v.ctrl[CTRL_STEP_LO] |
+                         ((long long)v.ctrl[CTRL_STEP_HI] << 32);
+  uint32_t r_st[kSlotsPerThread], r_key[kSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int i = (int)threadIdx.x + j * RT;
+    r_st[j] = 0xffffffffu;
+    r_key[j] = 0xffffffffu;
+    if (i < n) {
+      r_st[j] = (uint32_t)v.stamp[i];
+      r_key[j] = (uint32_t)v.key_of[i];
+    }
   }
   __syncthreads();
+
+  // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
+  // the experts of rank < K are the selection, in order.
   for (int i = threadIdx.x; i < T * E; i += RT) {
     const int t = i / E, e = i - t * E;
     const double z = s_z[i];
@@ -227,6 +270,12 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     s_off[nU] = run;
     v.offset[nU] = run;
   }
+  // classification against the layer's slot_of row (in LDS)
+  for (int u = threadIdx.x; u < nU; u += RT) {
+    int sl = s_srow[s_U[u]];
+    s_uslot[u] = sl;
+    s_hit[u] = sl >= 0 ? 1 : 0;
+  }
   __syncthreads();
   // per-expert assignment lists, ascending token inside an expert
   for (int i = threadIdx.x; i < A; i += RT) {
@@ -239,15 +288,6 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     v.row_tok[pos] = i / K;
     v.row_w[pos] = s_tk_w[i];
   }
-
-  // classification
-  const int layer = a.layer;
-  for (int u = threadIdx.x; u < nU; u += RT) {
-    int sl = v.slot_of[layer * E + s_U[u]];
-    s_uslot[u] = sl;
-    s_hit[u] = sl >= 0 ? 1 : 0;
-  }
-  __syncthreads();
   const int nHit = block_compact(
       nU, [&](int u) { return s_hit[u] != 0; },
       [&](int u, int pos) {
@@ -263,19 +303,18 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
       },
       s_tmp);
 
-  // LRU victims
-  const int n = v.ctrl[CTRL_N];
-  const int C = v.ctrl[CTRL_C];
+  // LRU victims: the `need` smallest (stamp, key) among occupied slots not used this step
   const int nfree = C - n;
   const int need = nMiss > nfree ? nMiss - nfree : 0;
-  const long long step = (long long)(unsigned)v.ctrl[CTRL_STEP_LO] |
-                         ((long long)v.ctrl[CTRL_STEP_HI] << 32);
   __shared__ int s_err;
   if (threadIdx.x == 0) s_err = 0;
   if (need > 0) {
     const uint64_t NONE = ~0ull;
-    for (int i = threadIdx.x; i < n; i += RT)
-      s_comp[i] = ((uint64_t)(uint32_t)v.stamp[i] << 32) | (uint32_t)v.key_of[i];
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int i = (int)threadIdx.x + j * RT;
+      if (i < n) s_comp[i] = ((uint64_t)r_st[j] << 32) | r_key[j];
+    }
     __syncthreads();
     for (int u = threadIdx.x; u < nU; u += RT)  // keys of this step are never victims
       if (s_hit[u]) s_comp[s_uslot[u]] = NONE;
@@ -311,6 +350,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
       const int take = g < need - got ? g : need - got;
       for (int q = threadIdx.x; q < take; q += RT) {
         s_vict[got + q] = s_sorted[q];
+        s_vkey[got + q] = (int)(uint32_t)s_comp[s_sorted[q]];
         s_comp[s_sorted[q]] = NONE;
       }
       got += take;
@@ -333,7 +373,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   for (int i = threadIdx.x; i < nMiss; i += RT) {
     int slot = i < nfree ? n + i : s_vict[i - nfree];
     s_aslot[i] = slot;
-    s_avkey[i] = i < nfree ? -1 : v.key_of[slot];
+    s_avkey[i] = i < nfree ? -1 : s_vkey[i - nfree];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nMiss; i += RT)
@@ -386,9 +426,9 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
 size_t route_plan_lds_bytes(const Dims& d) {
   size_t b = sizeof(uint64_t) * (size_t)d.max_capacity;
   b += sizeof(double) * (size_t)d.max_tokens * d.E;
-  b += sizeof(int) * 2 * (size_t)d.E;
+  b += sizeof(int) * 3 * (size_t)d.E;
   b += (sizeof(int) + sizeof(float) + sizeof(double)) * (size_t)d.amax;
-  b += sizeof(int) * (size_t)(11 * d.umax + 1);
+  b += sizeof(int) * (size_t)(12 * d.umax + 1);
   return (b + 15) & ~(size_t)15;
 }
 
