@@ -132,7 +132,7 @@ def main() -> None:
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0 = workload's)")
     ap.add_argument("--groups", type=int, default=0,
                     help="fill groups per step on a side stream (0: whole step on one stream)")
-    ap.add_argument("--profile-every", type=int, default=8,
+    ap.add_argument("--profile-every", type=int, default=7,
                     help="time one gate/up launch in this many during the timed region")
     ap.add_argument("--cache-frac", type=float, default=0.0,
                     help="override the cache fraction (1.0: every expert fits, FFN alone)")

@@ -12,17 +12,18 @@
 
 namespace moe {
 hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const void* wr,
-                             int* out_idx, float* out_w, int layer, int T, hipStream_t s);
+                             int* out_idx, float* out_w, int layer, int T, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1);
 size_t route_plan_lds_bytes(const Dims& d);
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
                              int T, int max_entries, int with_combine, int stage,
-                             int count_timed, hipStream_t s);
+                             hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 int decode_ntok(int T);
 int down_columns_per_block(int fmt);
 int down_row_splits(int inter);
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
-                       int ngroups, int grid, hipStream_t s);
+                       int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 hipError_t launch_init(const Dev& v, int max_capacity, int n_keys, int capacity, hipStream_t s);
 hipError_t launch_resize(const Dev& v, int new_capacity, int max_capacity, int E,
                          const void* old_arena, void* new_arena, long long S, hipStream_t s);
@@ -164,7 +165,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-// Timing of the library's own launches with event pairs from a reusable ring.
+// Timing of the library's own launches with event pairs from a reusable ring; the events
+// are handed to the kernel dispatch (start and end of the kernel, no marker packets).
 struct Profiler {
   enum Kind { ROUTE = 0, FILL = 1, GATE_UP = 2, DOWN = 3, NKIND = 4 };
   static constexpr int kRing = 4096;
@@ -210,16 +212,14 @@ struct Profiler {
   }
   template <class F>
   hipError_t timed(int k, hipStream_t s, F launch) {
-    if (!(mask >> k & 1)) return launch(false);
-    if (seen[k]++ % every != 0) return launch(false);
+    if (!(mask >> k & 1)) return launch(nullptr, nullptr);
+    if (seen[k]++ % every != 0) return launch(nullptr, nullptr);
     if (pending == (size_t)kRing) {
       hipError_t e = harvest_one();
       if (e != hipSuccess) return e;
     }
     const size_t i = head;
-    hipError_t e = hipEventRecord(a[i], s);
-    if (e == hipSuccess) e = launch(true);
-    if (e == hipSuccess) e = hipEventRecord(b[i], s);
+    hipError_t e = launch(a[i], b[i]);  // the kernel dispatch itself takes both timestamps
     if (e != hipSuccess) return e;
     kind[i] = k;
     head = (head + 1) % kRing;
@@ -391,8 +391,8 @@ moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t
   if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
   if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = c->prof.timed(Profiler::ROUTE, s, [&](bool) {
-    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
+  hipError_t e = c->prof.timed(Profiler::ROUTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s, e0, e1);
   });
   if (e == hipSuccess) e = hipEventRecord(c->ev_plan, s);
   if (e != hipSuccess) return hip_fail(c, e);
@@ -411,8 +411,8 @@ moe_status moe_fill_misses(moe_cache c, int32_t groups, void* fill_stream) {
   // the victim slots.
   hipError_t e = hipStreamWaitEvent(s, c->ev_plan, 0);
   for (int g = 0; g < groups && e == hipSuccess; ++g) {
-    e = c->prof.timed(Profiler::FILL, s, [&](bool) {
-      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s);
+    e = c->prof.timed(Profiler::FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s, e0, e1);
     });
     if (e == hipSuccess) e = hipEventRecord(c->ev_fill[g], s);
   }
@@ -435,14 +435,14 @@ moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
   const int G = c->fill_groups;
   hipError_t e = hipSuccess;
   auto both = [&](int sel, int g, int ngroups, int max_entries, int with_combine) {
-    hipError_t r = P.timed(Profiler::GATE_UP, s, [&](bool timed) {
+    hipError_t r = P.timed(Profiler::GATE_UP, s, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
-                               max_entries, with_combine, 0, timed, s);
+                               max_entries, with_combine, 0, s, e0, e1);
     });
     if (r != hipSuccess) return r;
-    return P.timed(Profiler::DOWN, s, [&](bool timed) {
+    return P.timed(Profiler::DOWN, s, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
-                               max_entries, with_combine, 1, timed, s);
+                               max_entries, with_combine, 1, s, e0, e1);
     });
   };
   if (T > 0)  // hit experts and the shared expert: no fill to wait for
@@ -466,23 +466,23 @@ static moe_status layer_step_serial(moe_cache c, int32_t layer, const void* x, i
     return MOE_E_INVALID;
   if (c->d.has_shared && T > 0 && !aligned16(shared_blob)) return MOE_E_INVALID;
   auto& P = c->prof;
-  hipError_t e = P.timed(Profiler::ROUTE, s, [&](bool) {
-    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s);
+  hipError_t e = P.timed(Profiler::ROUTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s, e0, e1);
   });
   if (e == hipSuccess)
-    e = P.timed(Profiler::FILL, s, [&](bool) {
-      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, s);
+    e = P.timed(Profiler::FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, s, e0, e1);
     });
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
   if (e == hipSuccess && T > 0)
-    e = P.timed(Profiler::GATE_UP, s, [&](bool timed) {
+    e = P.timed(Profiler::GATE_UP, s, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 2, 0, 1, T,
-                               nu + c->d.has_shared, 1, 0, timed, s);
+                               nu + c->d.has_shared, 1, 0, s, e0, e1);
     });
   if (e == hipSuccess && T > 0)
-    e = P.timed(Profiler::DOWN, s, [&](bool timed) {
+    e = P.timed(Profiler::DOWN, s, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 2, 0, 1, T,
-                               nu + c->d.has_shared, 1, 1, timed, s);
+                               nu + c->d.has_shared, 1, 1, s, e0, e1);
     });
   if (e != hipSuccess) return hip_fail(c, e);
   c->plan_T = T;

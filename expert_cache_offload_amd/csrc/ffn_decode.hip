@@ -499,40 +499,43 @@ int decode_ntok(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
 template <class Kern>
 static hipError_t launch_with_lds(Kern kernel, int grid, size_t lds, const FfnArgs& a,
-                                  hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
+                                  hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (grid <= 0) {  // nothing to run; keep the timing events valid
+    hipError_t e = e0 ? hipEventRecord(e0, s) : hipSuccess;
+    if (e == hipSuccess && e1) e = hipEventRecord(e1, s);
+    return e;
+  }
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(FT), lds, s, a);
-  return hipGetLastError();
+  return launch_timed(kernel, dim3(grid), dim3(FT), lds, s, e0, e1, a);
 }
 
 // stage 0: the gate/up kernel; stage 1: the down kernel (+ combine when a.NC > 0)
 template <int FMT, int NTOK>
-static hipError_t launch_ffn(const FfnArgs& a, int stage, hipStream_t s) {
+static hipError_t launch_ffn(const FfnArgs& a, int stage, hipStream_t s, hipEvent_t e0,
+                             hipEvent_t e1) {
   const Dims& d = a.d;
   constexpr int HC = down_hc<FMT>();
-  if (stage == 0) return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA), 0, a, s);
+  if (stage == 0)
+    return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA), 0, a, s, e0, e1);
   hipError_t e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
-                                 sizeof(float) * (size_t)4 * NTOK * HC, a, s);
-  if (e != hipSuccess) return e;
-  if (a.NC > 0) {
-    hipLaunchKernelGGL(combine_kernel, dim3(a.NC), dim3(FT), 0, s, a);
-    e = hipGetLastError();
-  }
-  return e;
+                                 sizeof(float) * (size_t)4 * NTOK * HC, a, s, e0,
+                                 a.NC > 0 ? nullptr : e1);
+  if (e != hipSuccess || a.NC <= 0) return e;
+  return launch_timed(combine_kernel, dim3(a.NC), dim3(FT), 0, s, nullptr, e1, a);
 }
 
 template <int FMT>
-static hipError_t launch_fmt(const FfnArgs& a, int ntok, int stage, hipStream_t s) {
+static hipError_t launch_fmt(const FfnArgs& a, int ntok, int stage, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1) {
   switch (ntok) {
-    case 1: return launch_ffn<FMT, 1>(a, stage, s);
-    case 2: return launch_ffn<FMT, 2>(a, stage, s);
-    case 4: return launch_ffn<FMT, 4>(a, stage, s);
-    default: return launch_ffn<FMT, 8>(a, stage, s);
+    case 1: return launch_ffn<FMT, 1>(a, stage, s, e0, e1);
+    case 2: return launch_ffn<FMT, 2>(a, stage, s, e0, e1);
+    case 4: return launch_ffn<FMT, 4>(a, stage, s, e0, e1);
+    default: return launch_ffn<FMT, 8>(a, stage, s, e0, e1);
   }
 }
 
@@ -553,20 +556,20 @@ int down_row_splits(int inter) {
 // sel 2: every entry of the step (hits, shared, misses).  max_entries bounds the entries of
 // the launch; with_combine adds the combine kernel after the down kernel (only on the step's
 // last launch); stage 0 launches the gate/up kernel, stage 1 the down kernel (and the
-// combine).
+// combine).  e0/e1 (nullable) take the start of the first and the end of the last kernel.
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
                              int T, int max_entries, int with_combine, int stage,
-                             int count_timed, hipStream_t s) {
+                             hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int nc = with_combine ? T * ((d.H + FT - 1) / FT) : 0;
   FfnArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
             (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
-            max_entries > 0 ? max_entries : 0, nc, count_timed};
+            max_entries > 0 ? max_entries : 0, nc, e0 != nullptr};
   const int ntok = decode_ntok(T);
   switch (d.fmt) {
-    case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, stage, s);
-    case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, stage, s);
-    default: return launch_fmt<FMT_MXFP4>(a, ntok, stage, s);
+    case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, stage, s, e0, e1);
+    case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, stage, s, e0, e1);
+    default: return launch_fmt<FMT_MXFP4>(a, ntok, stage, s, e0, e1);
   }
 }
 

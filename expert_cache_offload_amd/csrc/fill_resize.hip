@@ -63,10 +63,9 @@ __global__ __launch_bounds__(FILL_THREADS) void fill_kernel(FillArgs a) {
 }
 
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
-                       int ngroups, int grid, hipStream_t s) {
+                       int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   FillArgs a{v, (const uint4*)pool_dev, (uint4*)arena, S / 16, group, ngroups};
-  hipLaunchKernelGGL(fill_kernel, dim3(grid), dim3(FILL_THREADS), 0, s, a);
-  return hipGetLastError();
+  return launch_timed(fill_kernel, dim3(grid), dim3(FILL_THREADS), 0, s, e0, e1, a);
 }
 
 // ---------------------------------------------------------------- state init

@@ -11,6 +11,7 @@
 //   count[umax], offset[umax+1], perm/inv_pos/tk_idx/tk_w[amax], logits[max_tokens*E],
 //   FFN intermediates (act) and per-expert outputs (yexp).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,6 +38,18 @@ enum : int {
 };
 enum : int { ERR_CAPACITY = 1 };
 constexpr int kMaxSlots = 4096;  // most cache slots a handle supports (LDS-resident LRU)
+
+// Launch with optional timing events taken by the dispatch itself (start/end of the kernel,
+// no extra packets in the queue); plain launch when both are null.
+template <class K, class... Args>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                               hipEvent_t e0, hipEvent_t e1, Args... args) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
 enum : int {
   STAT_STEPS = 0,
   STAT_HITS = 1,

@@ -433,11 +433,12 @@ size_t route_plan_lds_bytes(const Dims& d) {
 }
 
 hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const void* wr,
-                             int* out_idx, float* out_w, int layer, int T, hipStream_t s) {
+                             int* out_idx, float* out_w, int layer, int T, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1) {
   RouteArgs a{d, v, (const uint16_t*)x, (const uint16_t*)wr, out_idx, out_w, layer, T};
   int grid = (d.E + (RT / 64) - 1) / (RT / 64);
-  hipLaunchKernelGGL(route_plan_kernel, dim3(grid), dim3(RT), route_plan_lds_bytes(d), s, a);
-  return hipGetLastError();
+  return launch_timed(route_plan_kernel, dim3(grid), dim3(RT), route_plan_lds_bytes(d), s, e0, e1,
+                      a);
 }
 
 }  // namespace moe
