@@ -123,6 +123,125 @@ def _traffic_from_profile(name: str) -> float | None:
     return val if src_ok else None
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def cpu_baseline_prefill(wb, tokens: int) -> dict:
+    """The float64 oracle on the first `tokens` tokens of the chunk through the first layer
+    (route, top-k, dedup, LRU and the SwiGLU FFN), scaled to the whole layer stack."""
+    from threadpoolctl import threadpool_info
+
+    import dataclasses
+    from oracle.step import Oracle
+    wl = dataclasses.replace(wb.wl, tokens_per_step=tokens)
+    orc = Oracle(wl, wb.pool, wb.router_np)
+    t0 = time.perf_counter()
+    orc.layer_step(0, 0, wb.acts_np[0][:tokens], True)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": tokens / (dt * wb.wl.layers), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {tokens} tokens of the chunk through layer 0 (full float64 route, "
+                      f"top-k, dedup, LRU, SwiGLU FFN), {dt:.1f} s, scaled to "
+                      f"{wb.wl.layers} layers",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def run_prefill(args, wl) -> None:
+    """Prefill chunks through the layer stack from a cold cache: tokens/s, the matrix-core
+    FFN against the bf16 MFMA roofline, fills against pinned hipMemcpyAsync, and the same
+    chunk without double buffering (fills and FFN in stream order)."""
+    import torch
+
+    from expert_cache_offload_amd import (PROF_DOWN, PROF_FILL, PROF_GATE_UP, moe_profile_enable,
+                                          moe_profile_read)
+    from expert_cache_offload_amd.runner import Workbench
+
+    groups = args.groups if args.groups > 0 else 16
+    steps = args.steps if args.steps_given else 2
+    warmup = args.warmup if args.warmup_given else 1
+    T, L, H, I, K = wl.tokens_per_step, wl.layers, wl.hidden, wl.inter, wl.top_k
+    print(f"[bench] prefill {wl.name}: L={L} T={T} H={H} E={wl.experts} k={K} I={I} "
+          f"C={wl.capacity} pool={wl.pool_bytes / 1e9:.2f} GB, {groups} fill groups",
+          file=sys.stderr, flush=True)
+    wb = Workbench(wl, groups=groups, max_capacity=wl.capacity)
+
+    def chunk(g: int) -> float:
+        wb.groups = g
+        wb.reset()
+        t0 = time.perf_counter()
+        for l in range(L):
+            wb.step(0, l)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    for _ in range(warmup):
+        chunk(groups)
+    times = []
+    for i in range(steps):
+        times.append(chunk(groups))
+        print(f"[bench] chunk {i}: {times[-1]:.3f} s", file=sys.stderr, flush=True)
+    wall = sum(times)
+    tok_s = steps * T / wall
+    # one more chunk with the FFN kernels and fills timed (event pairs on the dispatches)
+    wb.groups = groups
+    wb.reset()
+    moe_profile_enable(wb.handle, PROF_GATE_UP | PROF_DOWN | PROF_FILL, 1)
+    for l in range(L):
+        wb.step(0, l)
+    torch.cuda.synchronize()
+    prof = moe_profile_read(wb.handle)
+    st = wb.stats()
+    serial = chunk(0)
+    fl_gu = 2.0 * T * K * (2 * I) * H * L  # gate/up FLOPs of the chunk (every routed row)
+    fl_dn = 2.0 * T * K * I * H * L
+    gu_s = prof["gate_up"]["ms"] / 1e3
+    dn_s = prof["down"]["ms"] / 1e3
+    achieved = fl_gu / gu_s / 1e12 if gu_s > 0 else 0.0
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=wb.dev)
+    h2d = h2d_memcpy_probe(wb.pool_addr, wb.pool_bytes, wl.blob_bytes, scratch.data_ptr(),
+                           scratch.numel())
+    del scratch
+    fill_bytes = prof["fill_bytes"]
+    fk_s = prof["fill"]["ms"] / 1e3
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_prefill(wb, 512)
+        print(f"[bench] oracle {cpu['value']:.2f} tok/s ({cpu['seconds']:.1f} s)",
+              file=sys.stderr, flush=True)
+    misses = st["misses"]
+    wb.close()
+    line = {
+        "metric": "MoE prefill tokens/s per layer stack (cold cache) + MFMA TFLOP/s fraction; "
+                  "miss-fill PCIe GB/s",
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "hidden": H, "experts": wl.experts,
+                   "top_k": K, "inter": I, "cache_slots": wl.capacity,
+                   "pool_bytes": wl.pool_bytes, "tokens_per_step": T, "fill_groups": groups,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "ffn_prefill_gate_up_kernel",
+                     "launches": prof["gate_up"]["launches"],
+                     "avg_launch_us": round(prof["gate_up"]["ms"] * 1e3 /
+                                            max(1, prof["gate_up"]["launches"]), 1),
+                     "algorithmic_flops_per_chunk": fl_gu},
+        "down_kernel_TFLOPs": round(fl_dn / dn_s / 1e12, 1) if dn_s > 0 else None,
+        "cpu_baseline": cpu,
+        "fill": {"bytes_per_chunk": fill_bytes, "misses_per_chunk": misses,
+                 "kernel_GBps": round(fill_bytes / fk_s / 1e9, 2) if fk_s > 0 else None,
+                 "h2d_memcpy_blob_GBps": round(h2d["blob_GBps"], 2),
+                 "h2d_memcpy_1GiB_GBps": round(h2d["large_GBps"], 2)},
+        "ablation": {"double_buffered_s": round(min(times), 4), "serial_s": round(serial, 4),
+                     "serial_over_double_buffered": round(serial / min(times), 4)},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +261,8 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events")
     args = ap.parse_args()
+    args.steps_given = "--steps" in sys.argv
+    args.warmup_given = "--warmup" in sys.argv
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         _die_multi_gpu(max(args.gpus, world))
@@ -161,7 +282,8 @@ def main() -> None:
     n_tok = args.warmup + args.steps
     n_all = n_tok + args.breakdown_steps
     if wl.kind != "decode":
-        raise SystemExit("bench.py times decode workloads")
+        run_prefill(args, wl)
+        return
     wl = wl.with_steps(max(n_all, args.cpu_tokens))
     print(f"[bench] workload {wl.name}: L={wl.layers} H={wl.hidden} E={wl.experts} k={wl.top_k} "
           f"I={wl.inter} fmt={wl.fmt} C={wl.capacity} pool={wl.pool_bytes / 1e9:.2f} GB",

@@ -28,6 +28,14 @@ hipError_t launch_init(const Dev& v, int max_capacity, int n_keys, int capacity,
 hipError_t launch_resize(const Dev& v, int new_capacity, int max_capacity, int E,
                          const void* old_arena, void* new_arena, long long S, hipStream_t s);
 size_t resize_lds_bytes(int max_capacity);
+hipError_t launch_route_prefill(const Dims& d, const Dev& v, const void* x, const void* wr,
+                                int* out_idx, float* out_w, int layer, int T, hipStream_t s,
+                                hipEvent_t e0, hipEvent_t e1);
+bool prefill_route_supported(const Dims& d);
+hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const void* arena,
+                              const void* shared_blob, void* y, int sel, int group, int ngroups,
+                              int T, int stage, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+bool prefill_ffn_supported(const Dims& d);
 }  // namespace moe
 
 using namespace moe;
@@ -45,7 +53,8 @@ enum class State { Idle, Planned, Filled };
 struct Layout {
   size_t key_of, stamp, slot_of, ctrl, stats, hdr, U, u_slot, u_hit, hit_list, miss_list,
       miss_key, miss_slot, miss_victim, count, offset, perm, inv_pos, tk_idx, tk_w, logits,
-      act, act_shared, yexp, yexp_shared, ent, row_tok, row_w, moves, total;
+      act, act_shared, yexp, yexp_shared, ent, row_tok, row_w, moves, blk_cnt, blk_off, brank,
+      pact, pact_shared, pyexp, pyexp_shared, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -63,6 +72,9 @@ Dims make_dims(const moe_shape& s, int max_capacity) {
   d.max_tokens = s.max_tokens;
   d.amax = s.max_tokens * s.top_k;
   d.umax = d.amax < s.experts ? d.amax : s.experts;
+  d.tdec = s.max_tokens < kDecodeMaxTokens ? s.max_tokens : kDecodeMaxTokens;
+  d.adec = d.tdec * s.top_k;
+  d.nblk = s.max_tokens > kDecodeMaxTokens ? (s.max_tokens + 63) / 64 : 0;
   d.max_capacity = max_capacity;
   d.RS = down_row_splits(s.inter);
   d.S = s.blob_bytes;
@@ -98,15 +110,24 @@ Layout make_layout(const Dims& d) {
   L.inv_pos = take(I4 * d.amax);
   L.tk_idx = take(I4 * d.amax);
   L.tk_w = take(sizeof(float) * d.amax);
-  L.logits = take(sizeof(double) * (size_t)d.max_tokens * d.E);
-  L.act = take(sizeof(float) * (size_t)d.amax * d.I);
-  L.act_shared = take(d.has_shared ? sizeof(float) * (size_t)d.max_tokens * d.I : 256);
-  L.yexp = take(sizeof(float) * (size_t)d.amax * d.RS * d.H);
-  L.yexp_shared = take(d.has_shared ? sizeof(float) * (size_t)d.max_tokens * d.RS * d.H : 256);
+  L.logits = take(sizeof(double) * (size_t)d.tdec * d.E);
+  L.act = take(sizeof(float) * (size_t)d.adec * d.I);
+  L.act_shared = take(d.has_shared ? sizeof(float) * (size_t)d.tdec * d.I : 256);
+  L.yexp = take(sizeof(float) * (size_t)d.adec * d.RS * d.H);
+  L.yexp_shared = take(d.has_shared ? sizeof(float) * (size_t)d.tdec * d.RS * d.H : 256);
   L.ent = take(sizeof(int) * 4 * (size_t)d.umax);
   L.row_tok = take(I4 * d.amax);
   L.row_w = take(sizeof(float) * d.amax);
   L.moves = take(I4 * 2 * (size_t)d.max_capacity);
+  const bool many = d.nblk > 0;  // buffers of steps with more than eight tokens
+  const size_t T = many ? (size_t)d.max_tokens : 0, A = many ? (size_t)d.amax : 0;
+  L.blk_cnt = take(I4 * (size_t)d.nblk * d.E);
+  L.blk_off = take(I4 * (size_t)d.nblk * d.E);
+  L.brank = take(I4 * A);
+  L.pact = take(sizeof(uint16_t) * A * d.I);
+  L.pact_shared = take(d.has_shared ? sizeof(uint16_t) * T * d.I : 0);
+  L.pyexp = take(sizeof(float) * A * d.H);
+  L.pyexp_shared = take(d.has_shared ? sizeof(float) * T * d.H : 0);
   L.total = o;
   return L;
 }
@@ -143,6 +164,13 @@ Dev make_dev(void* ws, const Layout& L) {
   v.row_tok = (int*)(b + L.row_tok);
   v.row_w = (float*)(b + L.row_w);
   v.moves = (int*)(b + L.moves);
+  v.blk_cnt = (int*)(b + L.blk_cnt);
+  v.blk_off = (int*)(b + L.blk_off);
+  v.brank = (int*)(b + L.brank);
+  v.pact = (uint16_t*)(b + L.pact);
+  v.pact_shared = (uint16_t*)(b + L.pact_shared);
+  v.pyexp = (float*)(b + L.pyexp);
+  v.pyexp_shared = (float*)(b + L.pyexp_shared);
   return v;
 }
 
@@ -154,7 +182,7 @@ bool shape_ok(const moe_shape* s) {
   if (s->inter < 128 || s->inter % 128) return false;
   if (s->wfmt < 0 || s->wfmt > 2) return false;
   if (s->has_shared != 0 && s->has_shared != 1) return false;
-  if (s->max_tokens < 1 || s->max_tokens > kDecodeMaxTokens) return false;
+  if (s->max_tokens < 1 || s->max_tokens > kMaxTokens) return false;
   if (s->blob_bytes != moe_blob_bytes(s->wfmt, s->hidden, s->inter)) return false;
   if (s->blob_bytes % 16) return false;
   if ((long long)s->layers * s->experts > (1ll << 30)) return false;
@@ -383,6 +411,48 @@ moe_status moe_cache_resize(moe_cache c, int32_t new_capacity, void* new_arena, 
   return MOE_OK;
 }
 
+// Steps of more than eight tokens take the tiled router and the matrix-core FFN.
+static bool many_tokens_ok(const Dims& d) {
+  return d.nblk > 0 && prefill_route_supported(d) && prefill_ffn_supported(d);
+}
+
+static hipError_t route_launch(moe_cache c, int layer, const void* x, int T, const void* wr,
+                               int* idx, float* w, hipStream_t s) {
+  return c->prof.timed(Profiler::ROUTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (T > kDecodeMaxTokens)
+      return launch_route_prefill(c->d, c->v, x, wr, idx, w, layer, T, s, e0, e1);
+    return launch_route_plan(c->d, c->v, x, wr, idx, w, layer, T, s, e0, e1);
+  });
+}
+
+// One FFN launch group (gate/up, down, and the combine when with_combine) over the entries
+// that sel / g / ngroups select.
+static hipError_t ffn_launch(moe_cache c, const void* x, int T, const void* shared_blob, void* y,
+                             int sel, int g, int ngroups, int max_entries, int with_combine,
+                             hipStream_t s) {
+  auto& P = c->prof;
+  const bool many = T > kDecodeMaxTokens;
+  hipError_t r = P.timed(Profiler::GATE_UP, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (many)
+      return launch_ffn_prefill(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T, 0,
+                                s, e0, e1);
+    return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
+                             max_entries, with_combine, 0, s, e0, e1);
+  });
+  if (r != hipSuccess) return r;
+  return P.timed(Profiler::DOWN, s, [&](hipEvent_t e0, hipEvent_t e1) {
+    if (many) {
+      hipError_t q = launch_ffn_prefill(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups,
+                                        T, 1, s, e0, with_combine ? nullptr : e1);
+      if (q != hipSuccess || !with_combine) return q;
+      return launch_ffn_prefill(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T, 2,
+                                s, nullptr, e1);
+    }
+    return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
+                             max_entries, with_combine, 1, s, e0, e1);
+  });
+}
+
 moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t T,
                               const void* w_router, int32_t* topk_idx, float* topk_w,
                               void* stream) {
@@ -390,10 +460,9 @@ moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t
   if (c->state != State::Idle) return MOE_E_INVALID;
   if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
   if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_E_INVALID;
+  if (T > kDecodeMaxTokens && !many_tokens_ok(c->d)) return MOE_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = c->prof.timed(Profiler::ROUTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
-    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s, e0, e1);
-  });
+  hipError_t e = route_launch(c, layer, x, T, w_router, topk_idx, topk_w, s);
   if (e == hipSuccess) e = hipEventRecord(c->ev_plan, s);
   if (e != hipSuccess) return hip_fail(c, e);
   c->state = State::Planned;
@@ -434,22 +503,13 @@ moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
   const int G = c->fill_groups;
   hipError_t e = hipSuccess;
-  auto both = [&](int sel, int g, int ngroups, int max_entries, int with_combine) {
-    hipError_t r = P.timed(Profiler::GATE_UP, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
-                               max_entries, with_combine, 0, s, e0, e1);
-    });
-    if (r != hipSuccess) return r;
-    return P.timed(Profiler::DOWN, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, sel, g, ngroups, T,
-                               max_entries, with_combine, 1, s, e0, e1);
-    });
-  };
+  (void)P;
   if (T > 0)  // hit experts and the shared expert: no fill to wait for
-    e = both(0, 0, 1, nu + c->d.has_shared, 0);
+    e = ffn_launch(c, x, T, shared_blob, y, 0, 0, 1, nu + c->d.has_shared, 0, s);
   for (int g = 0; g < G && e == hipSuccess; ++g) {
     e = hipStreamWaitEvent(s, c->ev_fill[g], 0);
-    if (e == hipSuccess && T > 0) e = both(1, g, G, (nu + G - 1) / G, g == G - 1);
+    if (e == hipSuccess && T > 0)
+      e = ffn_launch(c, x, T, shared_blob, y, 1, g, G, (nu + G - 1) / G, g == G - 1, s);
   }
   if (e != hipSuccess) return hip_fail(c, e);
   c->state = State::Idle;
@@ -466,24 +526,14 @@ static moe_status layer_step_serial(moe_cache c, int32_t layer, const void* x, i
     return MOE_E_INVALID;
   if (c->d.has_shared && T > 0 && !aligned16(shared_blob)) return MOE_E_INVALID;
   auto& P = c->prof;
-  hipError_t e = P.timed(Profiler::ROUTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
-    return launch_route_plan(c->d, c->v, x, w_router, topk_idx, topk_w, layer, T, s, e0, e1);
-  });
+  hipError_t e = route_launch(c, layer, x, T, w_router, topk_idx, topk_w, s);
   if (e == hipSuccess)
     e = P.timed(Profiler::FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
       return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, s, e0, e1);
     });
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
   if (e == hipSuccess && T > 0)
-    e = P.timed(Profiler::GATE_UP, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 2, 0, 1, T,
-                               nu + c->d.has_shared, 1, 0, s, e0, e1);
-    });
-  if (e == hipSuccess && T > 0)
-    e = P.timed(Profiler::DOWN, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_ffn_decode(c->d, c->v, x, c->arena, shared_blob, y, 2, 0, 1, T,
-                               nu + c->d.has_shared, 1, 1, s, e0, e1);
-    });
+    e = ffn_launch(c, x, T, shared_blob, y, 2, 0, 1, nu + c->d.has_shared, 1, s);
   if (e != hipSuccess) return hip_fail(c, e);
   c->plan_T = T;
   c->plan_layer = layer;
@@ -501,6 +551,7 @@ moe_status moe_layer_step(moe_cache c, int32_t layer, const void* x, int32_t T,
   if (layer < 0 || layer >= c->d.L || T < 0 || T > c->d.max_tokens) return MOE_E_INVALID;
   if (T > 0 && (!x || !y || !w_router)) return MOE_E_INVALID;
   if (c->d.has_shared && T > 0 && !shared_blob) return MOE_E_INVALID;
+  if (T > kDecodeMaxTokens && !many_tokens_ok(c->d)) return MOE_E_INVALID;
   if (groups == 0)
     return layer_step_serial(c, layer, x, T, w_router, shared_blob, topk_idx, topk_w, y,
                              (hipStream_t)compute_stream);

@@ -1,0 +1,375 @@
+// SwiGLU expert FFN for a step of many tokens: grouped GEMMs on the bf16 matrix cores.
+//
+// Same computation as at decode (y_t = sum_j w_tj * Wd_e (silu(Wg_e x_t) * (Wu_e x_t)) over
+// the token's top-k experts, plus a shared expert with weight 1 when the model has one),
+// with every expert's rows gathered in the expert-sorted order of the plan.  Hit experts
+// run first and each fill group as soon as its copy has landed ("FreeToken：在消费级
+// NVIDIA GPU 上进行 MoE 推理", section on the problems FreeToken solves: the next group
+// transfers while this group computes; the same page's measurements put the cost of
+// turning this overlap off at about a quarter of prefill speed).
+//
+// Gfx950 design.  Dense contractions on v_mfma_f32_32x32x16_bf16 (fp32 accumulation):
+//   gate/up  - tile = 128 rows x 64 intermediate rows; the 128 GEMM columns are the 64 gate
+//              rows and the 64 up rows, so each wave holds gate and up of the same
+//              (row, i) in the same lane and the epilogue a = silu(g) * u * w is per lane;
+//              rows are gathered from x by the plan's row -> token map; a is stored bf16;
+//   down     - tile = 128 rows x 128 output columns over the stored transpose WdT, whose
+//              rows are contraction rows: the B tile is transposed on its way into LDS;
+//              fp32 partial rows per (token, choice);
+//   combine  - y[t] = bf16(sum over the token's k rows (+ shared) in a fixed order).
+// Four waves per workgroup in a 2 x 2 arrangement (64 x 64 each: four 32 x 32 MFMA tiles),
+// a 32-wide contraction stage in LDS with the next stage's global loads in flight during
+// the MFMAs.  Workgroups are persistent over the launch's tiles, whose count depends on
+// the plan (read on the device): a prefix over the launch's entries maps a tile to its
+// expert, row tile and column tile.
+#include "moe_dev.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int PFT = 256;        // threads (4 waves)
+constexpr int BM = 128;         // rows per tile
+constexpr int BK = 32;          // contraction per LDS stage
+constexpr int LDK = BK + 8;     // padded LDS row (bf16): 80 bytes
+constexpr int GBI = 64;         // intermediate rows per gate/up tile
+constexpr int DBN = 128;        // output columns per down tile
+constexpr int kMaxEntriesPf = 1040;
+
+struct PfArgs {
+  Dims d;
+  Dev v;
+  const uint16_t* x;  // [T][H] bf16
+  const unsigned char* arena;
+  const unsigned char* shared_blob;
+  uint16_t* y;        // [T][H] bf16
+  int sel;            // 0: hits + shared, 1: miss group `group` of `ngroups`, 2: all
+  int group;
+  int ngroups;
+  int T;
+  int timed;
+};
+
+struct PfEntry {
+  const unsigned char* blob;
+  int rows;    // routed: tokens of the expert; shared: T
+  int row0;    // first expert-sorted row (routed) or 0 (shared)
+  bool shared;
+};
+
+__device__ __forceinline__ int pf_launch_entries(const PfArgs& a, int& first) {
+  const int nHit = a.v.hdr[HDR_NHIT], nMiss = a.v.hdr[HDR_NMISS];
+  const int nHS = nHit + a.d.has_shared;
+  if (a.sel == 0) {
+    first = 0;
+    return nHS;
+  }
+  if (a.sel == 2) {
+    first = 0;
+    return nHS + nMiss;
+  }
+  const int m0 = (int)((long long)a.group * nMiss / a.ngroups);
+  const int m1 = (int)((long long)(a.group + 1) * nMiss / a.ngroups);
+  first = nHS + m0;
+  return m1 - m0;
+}
+
+__device__ __forceinline__ PfEntry pf_entry(const PfArgs& a, int g) {
+  const int nHit = a.v.hdr[HDR_NHIT];
+  PfEntry en;
+  if (a.d.has_shared && g == nHit) {
+    en.blob = a.shared_blob;
+    en.rows = a.T;
+    en.row0 = 0;
+    en.shared = true;
+    return en;
+  }
+  const int4 e = a.v.ent[g < nHit ? g : g - a.d.has_shared];
+  en.blob = a.arena + (size_t)e.x * (size_t)a.d.S;
+  en.rows = e.y;
+  en.row0 = e.z;
+  en.shared = false;
+  return en;
+}
+
+// Row tiles of the launch's entries: s_mt[j] = first row tile of entry j (exclusive prefix),
+// s_mt[n] = total.  Returns n.
+__device__ int pf_tile_prefix(const PfArgs& a, int* s_mt, int& first) {
+  const int n = pf_launch_entries(a, first);
+  for (int j = threadIdx.x; j < n; j += PFT) {
+    const PfEntry en = pf_entry(a, first + j);
+    s_mt[j + 1] = (en.rows + BM - 1) / BM;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s_mt[0] = 0;
+    for (int j = 1; j <= n; ++j) s_mt[j] += s_mt[j - 1];
+  }
+  __syncthreads();
+  return n;
+}
+
+__device__ __forceinline__ int pf_find(const int* s_mt, int n, int mt) {
+  int lo = 0, hi = n - 1;  // last j with s_mt[j] <= mt
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_mt[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float pf_silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ uint16_t pf_bf16(float f) { return f32_to_bf16_rne(f); }
+
+// ---------------------------------------------------------------- gate / up
+__global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
+  __shared__ __align__(16) uint16_t As[BM * LDK];
+  __shared__ __align__(16) uint16_t Bs[2 * GBI * LDK];
+  __shared__ int s_mt[kMaxEntriesPf + 1];
+  const Dims& d = a.d;
+  const int H = d.H, I = d.I;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int first;
+  const int n = pf_tile_prefix(a, s_mt, first);
+  const int NT = I / GBI;
+  const int ntiles = s_mt[n] * NT;
+  // this thread's two 16-byte chunks of each stage: rows r and r + 64, columns c .. c + 8
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 8;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int j = pf_find(s_mt, n, mt);
+    const PfEntry en = pf_entry(a, first + j);
+    if (threadIdx.x == 0 && mt == s_mt[j] && nt == 0) {
+      atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
+      if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_BLOB_BYTES], (unsigned long long)d.S);
+    }
+    const int m0 = (mt - s_mt[j]) * BM;
+    const int i0 = nt * GBI;
+    // A rows (gathered tokens); rows past the expert's count read zeros
+    const uint16_t* arow[2];
+    bool aval[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = m0 + lr + 64 * h;
+      aval[h] = r < en.rows;
+      const int tok = !aval[h] ? 0 : en.shared ? r : a.v.row_tok[en.row0 + r];
+      arow[h] = a.x + (size_t)tok * H;
+    }
+    // B rows: tile column c < 64 is gate row i0 + c, c >= 64 is up row i0 + c - 64
+    const uint16_t* brow[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lr + 64 * h;
+      const int i = i0 + (c & 63);
+      brow[h] = (const uint16_t*)en.blob + (size_t)i * 2 * H + (c >= 64 ? H : 0);
+    }
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[rr][g][q] = 0.f;
+    uint4 ra[2], rb[2];
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = aval[h] ? *(const uint4*)(arow[h] + lc) : z4;
+      rb[h] = *(const uint4*)(brow[h] + lc);
+    }
+    for (int k0 = 0; k0 < H; k0 += BK) {
+      __syncthreads();  // the previous stage's MFMAs are done with the LDS tiles
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        *(uint4*)(As + (lr + 64 * h) * LDK + lc) = ra[h];
+        *(uint4*)(Bs + (lr + 64 * h) * LDK + lc) = rb[h];
+      }
+      __syncthreads();
+      if (k0 + BK < H) {  // next stage's loads overlap this stage's MFMAs
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ra[h] = aval[h] ? *(const uint4*)(arow[h] + k0 + BK + lc) : z4;
+          rb[h] = *(const uint4*)(brow[h] + k0 + BK + lc);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 16) {
+        const int ko = kk + 8 * (lane >> 5);
+        bf16x8_t af[2], bf[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          af[rr] = *(const bf16x8_t*)(As + (wm * 64 + rr * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          bf[g] = *(const bf16x8_t*)(Bs + (g * 64 + wn * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            acc[rr][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[g], acc[rr][g], 0, 0, 0);
+      }
+    }
+    // epilogue: lane holds column i = i0 + wn*32 + lane%32 for 16 rows of each row tile
+    const int i = i0 + wn * 32 + (lane & 31);
+    uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (r < en.rows) {
+          const float w = en.shared ? 1.0f : a.v.row_w[en.row0 + r];
+          const float val = pf_silu(acc[rr][0][q]) * acc[rr][1][q] * w;
+          act[(size_t)(en.row0 + r) * I + i] = pf_bf16(val);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down
+__global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
+  __shared__ __align__(16) uint16_t As[BM * LDK];
+  __shared__ __align__(16) uint16_t Bs[DBN * LDK];  // [column][contraction]
+  __shared__ int s_mt[kMaxEntriesPf + 1];
+  const Dims& d = a.d;
+  const int H = d.H, I = d.I;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int first;
+  const int n = pf_tile_prefix(a, s_mt, first);
+  const int NT = H / DBN;
+  const int ntiles = s_mt[n] * NT;
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 8;     // A: rows lr, lr + 64
+  const int bk = threadIdx.x >> 4, bc = (threadIdx.x & 15) * 8;    // B: k rows bk, bk + 16
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int mt = tile / NT, nt = tile - mt * NT;
+    const int j = pf_find(s_mt, n, mt);
+    const PfEntry en = pf_entry(a, first + j);
+    const int m0 = (mt - s_mt[j]) * BM;
+    const int n0 = nt * DBN;
+    const uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
+    const uint16_t* arow[2];
+    bool aval[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = m0 + lr + 64 * h;
+      aval[h] = r < en.rows;
+      arow[h] = act + (size_t)(en.row0 + (aval[h] ? r : 0)) * I;
+    }
+    const uint16_t* wdt = (const uint16_t*)en.blob + (size_t)2 * I * H;  // WdT [I][H]
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[rr][cc][q] = 0.f;
+    uint4 ra[2], rb[2];
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = aval[h] ? *(const uint4*)(arow[h] + lc) : z4;
+      rb[h] = *(const uint4*)(wdt + (size_t)(bk + 16 * h) * H + n0 + bc);
+    }
+    for (int k0 = 0; k0 < I; k0 += BK) {
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        *(uint4*)(As + (lr + 64 * h) * LDK + lc) = ra[h];
+        // transpose: 8 consecutive columns of contraction row k go to 8 LDS rows
+        const int k = bk + 16 * h;
+        const uint32_t w[4] = {rb[h].x, rb[h].y, rb[h].z, rb[h].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          Bs[(bc + 2 * q) * LDK + k] = (uint16_t)(w[q] & 0xffffu);
+          Bs[(bc + 2 * q + 1) * LDK + k] = (uint16_t)(w[q] >> 16);
+        }
+      }
+      __syncthreads();
+      if (k0 + BK < I) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ra[h] = aval[h] ? *(const uint4*)(arow[h] + k0 + BK + lc) : z4;
+          rb[h] = *(const uint4*)(wdt + (size_t)(k0 + BK + bk + 16 * h) * H + n0 + bc);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 16) {
+        const int ko = kk + 8 * (lane >> 5);
+        bf16x8_t af[2], bf[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+          af[rr] = *(const bf16x8_t*)(As + (wm * 64 + rr * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          bf[cc] = *(const bf16x8_t*)(Bs + (wn * 64 + cc * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+            acc[rr][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[cc], acc[rr][cc], 0, 0, 0);
+      }
+    }
+    float* yrow = en.shared ? a.v.pyexp_shared : a.v.pyexp;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (r < en.rows) {
+          float* out = yrow + (size_t)(en.row0 + r) * H + n0 + wn * 64 + (lane & 31);
+          out[0] = acc[rr][0][q];
+          out[32] = acc[rr][1][q];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+__global__ __launch_bounds__(PFT) void ffn_prefill_combine_kernel(PfArgs a) {
+  const Dims& d = a.d;
+  const int H = d.H, K = d.K;
+  const int per_tok = H / PFT;  // H is a multiple of 256
+  const int t = blockIdx.x / per_tok;
+  const int c = (blockIdx.x % per_tok) * PFT + threadIdx.x;
+  __shared__ int s_pos[16];
+  if ((int)threadIdx.x < K) s_pos[threadIdx.x] = a.v.inv_pos[t * K + threadIdx.x];
+  __syncthreads();
+  float pv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) pv[j] = j < K ? a.v.pyexp[(size_t)s_pos[j] * H + c] : 0.f;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += pv[j];
+  if (d.has_shared) s += a.v.pyexp_shared[(size_t)t * H + c];
+  a.y[(size_t)t * H + c] = f32_to_bf16_rne(s);
+}
+
+constexpr int kPfGrid = 1024;  // persistent workgroups per GEMM launch (4 per CU)
+
+// stage 0: gate/up; stage 1: down; stage 2: combine.  e0/e1 (nullable) time the launch.
+hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const void* arena,
+                              const void* shared_blob, void* y, int sel, int group, int ngroups,
+                              int T, int stage, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  PfArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
+           (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
+           e0 != nullptr};
+  if (stage == 0)
+    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
+  if (stage == 1)
+    return launch_timed(ffn_prefill_down_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
+  return launch_timed(ffn_prefill_combine_kernel, dim3(T * (d.H / PFT)), dim3(PFT), 0, s, e0, e1,
+                      a);
+}
+
+bool prefill_ffn_supported(const Dims& d) {
+  return d.fmt == FMT_BF16 && d.I % GBI == 0 && d.H % DBN == 0 && d.K <= 16 &&
+         d.umax + d.has_shared <= kMaxEntriesPf;
+}
+
+}  // namespace moe

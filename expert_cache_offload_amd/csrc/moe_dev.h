@@ -8,8 +8,9 @@
 //   stats[4]              steps, hits, misses, bytes filled
 // Per-step plan (rewritten by every route launch):
 //   hdr[16], U/u_slot/u_hit/hit_list/miss_list/miss_key/miss_slot/miss_victim[umax],
-//   count[umax], offset[umax+1], perm/inv_pos/tk_idx/tk_w[amax], logits[max_tokens*E],
-//   FFN intermediates (act) and per-expert outputs (yexp).
+//   count[umax], offset[umax+1], perm/inv_pos/tk_idx/tk_w[amax], logits[tdec*E],
+//   FFN intermediates (act) and per-expert outputs (yexp); for steps of more than eight
+//   tokens the block counts and offsets of the router and bf16 / fp32 row buffers.
 #pragma once
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -62,13 +63,17 @@ enum : int {
 
 constexpr int FMT_BF16 = 0, FMT_FP8 = 1, FMT_MXFP4 = 2;
 constexpr int kDecodeMaxTokens = 8;  // T handled by the GEMV decode path
+constexpr int kMaxTokens = 65536;    // most tokens of one layer step
 
 struct Dims {
   int L, E, K, H, I, fmt, has_shared, max_tokens;
   int umax;          // min(max_tokens*K, E): distinct experts per step
   int amax;          // max_tokens*K: (token, choice) assignments per step
+  int tdec;          // min(max_tokens, kDecodeMaxTokens): tokens of the decode path
+  int adec;          // tdec*K
+  int nblk;          // 64-token blocks of the many-token path (0 when max_tokens <= 8)
   int max_capacity;  // slots the arena holds
-  int RS;            // row splits of the down projection (1 or 2)
+  int RS;            // row splits of the decode down projection
   long long S;       // blob bytes
 };
 
@@ -94,10 +99,17 @@ struct Dev {
   int* tk_idx;
   float* tk_w;
   double* logits;
-  float* act;          // [amax][I] silu(g)*u*w per (expert, token) row
-  float* act_shared;   // [max_tokens][I] shared expert
-  float* yexp;         // [amax][RS][H] per (expert, token) output
-  float* yexp_shared;  // [max_tokens][RS][H] shared expert
+  float* act;          // [adec][I] silu(g)*u*w per (expert, token) row (decode)
+  float* act_shared;   // [tdec][I] shared expert (decode)
+  float* yexp;         // [adec][RS][H] per (expert, token) output (decode)
+  float* yexp_shared;  // [tdec][RS][H] shared expert (decode)
+  int* blk_cnt;        // [nblk][E] assignments per (64-token block, expert)
+  int* blk_off;        // [nblk][E] first expert-sorted row of each (block, expert)
+  int* brank;          // [amax] rank of a (token, choice) among its block's rows
+  uint16_t* pact;      // [amax][I] bf16 silu(g)*u*w per expert-sorted row (many tokens)
+  uint16_t* pact_shared;  // [max_tokens][I] shared expert
+  float* pyexp;        // [amax][H] fp32 expert output per row
+  float* pyexp_shared; // [max_tokens][H] shared expert output
   int4* ent;           // [umax] FFN entries in order hits, misses: {slot, ntok, row0, miss idx}
   int* row_tok;        // [amax] token of each expert-sorted assignment row
   float* row_w;        // [amax] routing weight of each row

@@ -1,0 +1,319 @@
+// The single-workgroup part of a layer step's plan, shared by the decode route kernel and
+// the prefill plan kernel: per-step dedup of the selected experts, hit/miss classification
+// against the (layer, expert)-keyed slot table, LRU victim selection and the slot-table
+// update, the FFN entry table, the plan header and the counters.
+//
+// FreeToken paper summary (agihunt.info, arXiv 2608.16157), execution-layer paragraph:
+// routing dedup, hit classification and LRU victim selection run on the GPU with no host
+// round trip; the cache is one slot pool shared by all MoE layers (memory-architecture
+// paragraph) with a global LRU (attribution paragraph).  The rule reproduced: U is the
+// ascending set of selected experts; misses are taken in ascending expert id; free slots
+// [n, C) go first in ascending order, then the `need` smallest (stamp, key) among occupied
+// slots not used by this step; every key of U is stamped with the step counter.
+#pragma once
+#include "moe_dev.h"
+
+namespace moe {
+
+constexpr int RT = 256;  // threads of a plan workgroup (4 waves)
+constexpr int kSlotsPerThread = kMaxSlots / RT;
+
+// Ordered compaction over [0, n): emit(i, pos) for every i with pred(i); pos ascends with i.
+template <class P, class F>
+__device__ int block_compact(int n, P pred, F emit, int* s_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int running = 0;
+  for (int base = 0; base < n; base += RT) {
+    int i = base + (int)threadIdx.x;
+    bool p = i < n && pred(i);
+    uint64_t b = __ballot(p);
+    if (lane == 0) s_tmp[wave] = __popcll(b);
+    __syncthreads();
+    int off = running;
+    for (int w = 0; w < wave; ++w) off += s_tmp[w];
+    int tot = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+    if (p) emit(i, off + (int)__popcll(b & lanemask_lt()));
+    running += tot;
+    __syncthreads();
+  }
+  return running;
+}
+
+__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_tmp) {
+  for (int off = 32; off > 0; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off);
+    v = o < v ? o : v;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) s_tmp[wave] = v;
+  __syncthreads();
+  uint64_t m = s_tmp[0];
+  for (int w = 1; w < RT / 64; ++w) m = s_tmp[w] < m ? s_tmp[w] : m;
+  __syncthreads();
+  return m;
+}
+
+// LDS arrays of the plan (dynamic shared memory).
+struct PlanLds {
+  uint64_t* comp;  // [max_capacity] (stamp << 32 | key) per occupied slot
+  int* cnt;        // [E] assignments per expert this step
+  int* uidx;       // [E] position of an expert in U, -1 if unused
+  int* srow;       // [E] this layer's row of slot_of
+  int* U;          // [umax] + the arrays below, per position in U unless noted
+  int* off;        // [umax + 1]
+  int* uslot;
+  int* hit;
+  int* miss;       // [umax] miss list (positions in U)
+  int* vict;       // [umax] victim slots in eviction order
+  int* vkey;       // [umax] their keys
+  int* grp;
+  int* sorted;
+  int* aslot;      // [umax] per miss: assigned slot
+  int* avkey;      // [umax] per miss: evicted key or -1
+  int* hitl;       // [umax] hit list (positions in U)
+};
+
+inline __host__ __device__ size_t plan_lds_bytes(const Dims& d) {
+  size_t b = sizeof(uint64_t) * (size_t)d.max_capacity;
+  b += sizeof(int) * 3 * (size_t)d.E;
+  b += sizeof(int) * (size_t)(12 * d.umax + 1);
+  return (b + 15) & ~(size_t)15;
+}
+
+__device__ inline unsigned char* plan_carve(const Dims& d, unsigned char* p, PlanLds& s) {
+  const int umax = d.umax;
+  s.comp = (uint64_t*)p;  p += sizeof(uint64_t) * d.max_capacity;
+  s.cnt = (int*)p;        p += sizeof(int) * d.E;
+  s.uidx = (int*)p;       p += sizeof(int) * d.E;
+  s.srow = (int*)p;       p += sizeof(int) * d.E;
+  s.U = (int*)p;          p += sizeof(int) * umax;
+  s.off = (int*)p;        p += sizeof(int) * (umax + 1);
+  s.uslot = (int*)p;      p += sizeof(int) * umax;
+  s.hit = (int*)p;        p += sizeof(int) * umax;
+  s.miss = (int*)p;       p += sizeof(int) * umax;
+  s.vict = (int*)p;       p += sizeof(int) * umax;
+  s.vkey = (int*)p;       p += sizeof(int) * umax;
+  s.grp = (int*)p;        p += sizeof(int) * umax;
+  s.sorted = (int*)p;     p += sizeof(int) * umax;
+  s.aslot = (int*)p;      p += sizeof(int) * umax;
+  s.avkey = (int*)p;      p += sizeof(int) * umax;
+  s.hitl = (int*)p;       p += sizeof(int) * umax;
+  return (unsigned char*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
+}
+
+// Static shared scratch of the plan.
+struct PlanTmp {
+  int tmp[8];
+  uint64_t tmp64[8];
+  int g;
+  int err;
+};
+
+// Cache state the plan reads, loaded once at its start.
+struct PlanState {
+  int n, C;
+  long long step;
+  uint32_t st[kSlotsPerThread], key[kSlotsPerThread];  // this thread's occupied slots
+};
+
+// All threads: reset the per-expert arrays, read this layer's slot_of row and the control
+// words, then the occupied slots' (stamp, key) into registers.  The caller syncs before
+// reading the LDS arrays.
+__device__ inline void plan_begin(const Dims& d, const Dev& v, int layer, PlanLds& s,
+                                  PlanState& ps) {
+  for (int e = threadIdx.x; e < d.E; e += RT) {
+    s.cnt[e] = 0;
+    s.uidx[e] = -1;
+    s.srow[e] = v.slot_of[layer * d.E + e];
+  }
+  ps.n = v.ctrl[CTRL_N];
+  ps.C = v.ctrl[CTRL_C];
+  ps.step = (long long)(unsigned)v.ctrl[CTRL_STEP_LO] | ((long long)v.ctrl[CTRL_STEP_HI] << 32);
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int i = (int)threadIdx.x + j * RT;
+    ps.st[j] = 0xffffffffu;
+    ps.key[j] = 0xffffffffu;
+    if (i < ps.n) {
+      ps.st[j] = (uint32_t)v.stamp[i];
+      ps.key[j] = (uint32_t)v.key_of[i];
+    }
+  }
+}
+
+// After s.cnt holds the step's assignments per expert (synced): U ascending (ballot /
+// popcount compaction), count/offset per position in U; returns nU.  Ends synced.
+__device__ inline int plan_dedup(const Dims& d, const Dev& v, PlanLds& s, PlanTmp& pt) {
+  const int nU = block_compact(
+      d.E, [&](int e) { return s.cnt[e] > 0; },
+      [&](int e, int pos) {
+        s.U[pos] = e;
+        s.uidx[e] = pos;
+        v.U[pos] = e;
+      },
+      pt.tmp);
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int u = 0; u < nU; ++u) {
+      s.off[u] = run;
+      v.offset[u] = run;
+      const int c = s.cnt[s.U[u]];
+      v.count[u] = c;
+      run += c;
+    }
+    s.off[nU] = run;
+    v.offset[nU] = run;
+  }
+  __syncthreads();
+  return nU;
+}
+
+// Classification, LRU victims, slot-table update, entry table, header and counters.
+// Returns false (after recording the error and an empty plan) when fewer slots can be
+// evicted than there are misses.
+__device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T, int nU,
+                                  PlanLds& s, const PlanState& ps, PlanTmp& pt) {
+  const int E = d.E, umax = d.umax;
+  for (int u = threadIdx.x; u < nU; u += RT) {
+    const int sl = s.srow[s.U[u]];
+    s.uslot[u] = sl;
+    s.hit[u] = sl >= 0 ? 1 : 0;
+  }
+  __syncthreads();
+  const int nHit = block_compact(
+      nU, [&](int u) { return s.hit[u] != 0; },
+      [&](int u, int pos) {
+        v.hit_list[pos] = u;
+        s.hitl[pos] = u;
+      },
+      pt.tmp);
+  const int nMiss = block_compact(
+      nU, [&](int u) { return s.hit[u] == 0; },
+      [&](int u, int pos) {
+        s.miss[pos] = u;
+        v.miss_list[pos] = u;
+      },
+      pt.tmp);
+
+  // LRU victims: the `need` smallest (stamp, key) among occupied slots not used this step,
+  // found in rounds of "oldest remaining stamp" (one round per distinct stamp taken: a
+  // step stamps all of its experts alike, so a group never exceeds umax)
+  const int n = ps.n, C = ps.C;
+  const int nfree = C - n;
+  const int need = nMiss > nfree ? nMiss - nfree : 0;
+  if (threadIdx.x == 0) pt.err = 0;
+  if (need > 0) {
+    const uint64_t NONE = ~0ull;
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int i = (int)threadIdx.x + j * RT;
+      if (i < n) s.comp[i] = ((uint64_t)ps.st[j] << 32) | ps.key[j];
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < nU; u += RT)  // keys of this step are never victims
+      if (s.hit[u]) s.comp[s.uslot[u]] = NONE;
+    __syncthreads();
+    int got = 0;
+    for (int round = 0; round < need && got < need; ++round) {
+      uint64_t m = NONE;
+      for (int i = threadIdx.x; i < n; i += RT) m = s.comp[i] < m ? s.comp[i] : m;
+      m = block_min_u64(m, pt.tmp64);
+      if (m == NONE) {  // fewer evictable slots than misses: capacity floor violated
+        if (threadIdx.x == 0) pt.err = 1;
+        break;
+      }
+      const uint32_t st = (uint32_t)(m >> 32);
+      if (threadIdx.x == 0) pt.g = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < n; i += RT) {
+        const uint64_t c = s.comp[i];
+        if (c != NONE && (uint32_t)(c >> 32) == st) {
+          const int q = atomicAdd(&pt.g, 1);
+          if (q < umax) s.grp[q] = i;
+        }
+      }
+      __syncthreads();
+      const int g = pt.g < umax ? pt.g : umax;
+      for (int q = threadIdx.x; q < g; q += RT) {  // order the group by key
+        const uint32_t kq = (uint32_t)s.comp[s.grp[q]];
+        int rank = 0;
+        for (int r = 0; r < g; ++r) rank += ((uint32_t)s.comp[s.grp[r]] < kq);
+        s.sorted[rank] = s.grp[q];
+      }
+      __syncthreads();
+      const int take = g < need - got ? g : need - got;
+      for (int q = threadIdx.x; q < take; q += RT) {
+        s.vict[got + q] = s.sorted[q];
+        s.vkey[got + q] = (int)(uint32_t)s.comp[s.sorted[q]];
+        s.comp[s.sorted[q]] = NONE;
+      }
+      got += take;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  if (pt.err) {
+    if (threadIdx.x == 0) {
+      atomicOr(&v.ctrl[CTRL_ERR], ERR_CAPACITY);
+      v.hdr[HDR_NU] = 0;
+      v.hdr[HDR_NHIT] = 0;
+      v.hdr[HDR_NMISS] = 0;
+    }
+    return false;
+  }
+
+  // slot assignment: free slots n, n+1, ... first, then victims in LRU order
+  for (int i = threadIdx.x; i < nMiss; i += RT) {
+    const int slot = i < nfree ? n + i : s.vict[i - nfree];
+    s.aslot[i] = slot;
+    s.avkey[i] = i < nfree ? -1 : s.vkey[i - nfree];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nMiss; i += RT)
+    if (s.avkey[i] >= 0) v.slot_of[s.avkey[i]] = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nMiss; i += RT) {
+    const int u = s.miss[i];
+    const int key = layer * E + s.U[u];
+    const int slot = s.aslot[i];
+    v.key_of[slot] = key;
+    v.slot_of[key] = slot;
+    s.uslot[u] = slot;
+    v.miss_key[i] = key;
+    v.miss_slot[i] = slot;
+    v.miss_victim[i] = s.avkey[i];
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < nU; u += RT) {
+    v.stamp[s.uslot[u]] = (int)ps.step;
+    v.u_slot[u] = s.uslot[u];
+    v.u_hit[u] = s.hit[u];
+  }
+  // FFN entry table: hits first, then misses in ascending expert id (the fill order)
+  for (int g = threadIdx.x; g < nU; g += RT) {
+    const int miss = g < nHit ? -1 : g - nHit;
+    const int u = miss < 0 ? s.hitl[g] : s.miss[miss];
+    v.ent[g] = make_int4(s.uslot[u], s.cnt[s.U[u]], s.off[u], miss);
+  }
+  if (threadIdx.x == 0) {
+    const int nn = n + nMiss;
+    v.ctrl[CTRL_N] = nn < C ? nn : C;
+    v.hdr[HDR_NU] = nU;
+    v.hdr[HDR_NHIT] = nHit;
+    v.hdr[HDR_NMISS] = nMiss;
+    v.hdr[HDR_LAYER] = layer;
+    v.hdr[HDR_T] = T;
+    v.hdr[HDR_STEP_LO] = (int)(ps.step & 0xffffffff);
+    v.hdr[HDR_STEP_HI] = (int)(ps.step >> 32);
+    const long long ns = ps.step + 1;
+    v.ctrl[CTRL_STEP_LO] = (int)(ns & 0xffffffff);
+    v.ctrl[CTRL_STEP_HI] = (int)(ns >> 32);
+    v.stats[STAT_STEPS] += 1;
+    v.stats[STAT_HITS] += (unsigned long long)nHit;
+    v.stats[STAT_MISSES] += (unsigned long long)nMiss;
+    v.stats[STAT_BYTES] += (unsigned long long)nMiss * (unsigned long long)d.S;
+  }
+  return true;
+}
+
+}  // namespace moe

@@ -108,6 +108,14 @@ class Workbench:
             self.arena = new_arena
         self.capacity = new_capacity
 
+    def reset(self) -> None:
+        """Start again from an empty cache (a new handle over the same arena and workspace)."""
+        self.sync()
+        moe_cache_destroy(self.handle)
+        self.handle = moe_cache_create(self.shape, self.capacity, self.max_capacity, self.arena,
+                                       self.ws, self.pool_addr, self.compute.cuda_stream)
+        self.sync()
+
     def sync(self) -> None:
         torch.cuda.synchronize(self.dev)
 

@@ -87,7 +87,7 @@ typedef struct {
   int32_t inter;      /* I, SwiGLU intermediate size, multiple of 128 */
   int32_t wfmt;       /* MOE_FMT_* */
   int32_t has_shared; /* 1: one GPU-resident shared expert per layer */
-  int32_t max_tokens; /* largest T passed to any step call, 1..8 */
+  int32_t max_tokens; /* largest T passed to any step call, 1..65536 (see below) */
   int64_t blob_bytes; /* must equal moe_blob_bytes(wfmt, hidden, inter) */
 } moe_shape;
 
@@ -146,9 +146,13 @@ moe_status moe_cache_destroy(moe_cache cache);
 moe_status moe_cache_resize(moe_cache cache, int32_t new_capacity, void* new_arena, void* stream);
 
 /* Router GEMM + top-k + dedup + classification + LRU victims + slot-table update
- * for `layer`, in one kernel on `stream`.  x: [T][hidden] bf16; w_router:
- * [experts][hidden] bf16.  topk_idx/topk_w may be NULL.  Writes the step plan into
- * the workspace; the next moe_fill_misses and moe_expert_ffn use it.
+ * for `layer` on `stream`.  x: [T][hidden] bf16; w_router: [experts][hidden] bf16.
+ * topk_idx/topk_w may be NULL.  Writes the step plan into the workspace; the next
+ * moe_fill_misses and moe_expert_ffn use it.
+ * Steps of up to 8 tokens (decode) run one fused kernel and the weight-streaming FFN;
+ * steps of more tokens (prefill chunks) run a tiled router (fp64 accumulation), a
+ * one-workgroup plan and a scatter, then the matrix-core FFN; they need bf16 weights,
+ * experts <= 256 and top_k <= 16 (MOE_E_INVALID otherwise).
  * MOE_E_INVALID if T > max_tokens, layer out of range, or the previous plan has
  * not had its FFN issued. */
 moe_status moe_route_classify(moe_cache cache, int32_t layer, const void* x, int32_t T,

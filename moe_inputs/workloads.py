@@ -83,6 +83,15 @@ class Workload:
     def with_steps(self, token_steps: int) -> "Workload":
         return dataclasses.replace(self, token_steps=token_steps)
 
+    def with_tokens(self, tokens: int) -> "Workload":
+        """Same shape with a different number of tokens per layer step."""
+        return dataclasses.replace(self, name=f"{self.name}_T{tokens}", tokens_per_step=tokens)
+
+    def as_prefill(self, tokens: int) -> "Workload":
+        """One chunk of `tokens` i.i.d. activations through the same layers and cache."""
+        return dataclasses.replace(self, name=f"{self.name}_prefill{tokens}", kind="prefill",
+                                   tokens_per_step=tokens, token_steps=1, resize_at=-1)
+
 
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 256, 16, 2, 128, 0, 0.0, 1, 64, "decode", fixed_capacity=8),
