@@ -28,11 +28,12 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // register-friendly 16 bytes
 
 constexpr int PFT = 256;        // threads (4 waves)
 constexpr int BM = 128;         // rows per tile
-constexpr int BK = 32;          // contraction per LDS stage
-constexpr int LDK = BK + 8;     // padded LDS row (bf16): 80 bytes
+constexpr int BK = 64;          // contraction per LDS stage (128-byte row segments)
+constexpr int LDK = BK + 8;     // padded LDS row (bf16): 144 bytes
 constexpr int GBI = 64;         // intermediate rows per gate/up tile
 constexpr int DBN = 128;        // output columns per down tile
 constexpr int kMaxEntriesPf = 1040;
@@ -121,6 +122,13 @@ __device__ __forceinline__ int pf_find(const int* s_mt, int n, int mt) {
 
 __device__ __forceinline__ float pf_silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Workgroups are dealt to the 8 XCDs round-robin; renumber them so that consecutive tiles
+// (the column tiles of one row tile, the row tiles of one expert) run on the same XCD and
+// meet their shared rows in that XCD's L2.  The grid is a multiple of 8.
+__device__ __forceinline__ int xcd_order() {
+  return (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8);
+}
+
 __device__ __forceinline__ uint16_t pf_bf16(float f) { return f32_to_bf16_rne(f); }
 
 // ---------------------------------------------------------------- gate / up
@@ -128,6 +136,7 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
   __shared__ __align__(16) uint16_t As[BM * LDK];
   __shared__ __align__(16) uint16_t Bs[2 * GBI * LDK];
   __shared__ int s_mt[kMaxEntriesPf + 1];
+  __shared__ float s_w[BM];  // routing weight of each row of the tile
   const Dims& d = a.d;
   const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -136,9 +145,9 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
   const int n = pf_tile_prefix(a, s_mt, first);
   const int NT = I / GBI;
   const int ntiles = s_mt[n] * NT;
-  // this thread's two 16-byte chunks of each stage: rows r and r + 64, columns c .. c + 8
-  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 8;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // this thread's 16-byte chunks of each stage: rows lr + 32 h (h < 4), columns lc .. lc + 8
+  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+  for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
     const PfEntry en = pf_entry(a, first + j);
@@ -148,21 +157,25 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
     }
     const int m0 = (mt - s_mt[j]) * BM;
     const int i0 = nt * GBI;
+    if ((int)threadIdx.x < BM) {  // read by the epilogue, after the k loop's barriers
+      const int r = m0 + threadIdx.x;
+      s_w[threadIdx.x] = r >= en.rows ? 0.f : en.shared ? 1.0f : a.v.row_w[en.row0 + r];
+    }
     // A rows (gathered tokens); rows past the expert's count read zeros
-    const uint16_t* arow[2];
-    bool aval[2];
+    const uint16_t* arow[4];
+    bool aval[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = m0 + lr + 64 * h;
+    for (int h = 0; h < 4; ++h) {
+      const int r = m0 + lr + 32 * h;
       aval[h] = r < en.rows;
       const int tok = !aval[h] ? 0 : en.shared ? r : a.v.row_tok[en.row0 + r];
       arow[h] = a.x + (size_t)tok * H;
     }
     // B rows: tile column c < 64 is gate row i0 + c, c >= 64 is up row i0 + c - 64
-    const uint16_t* brow[2];
+    const uint16_t* brow[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = lr + 64 * h;
+    for (int h = 0; h < 4; ++h) {
+      const int c = lr + 32 * h;
       const int i = i0 + (c & 63);
       brow[h] = (const uint16_t*)en.blob + (size_t)i * 2 * H + (c >= 64 ? H : 0);
     }
@@ -173,28 +186,30 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[rr][g][q] = 0.f;
-    uint4 ra[2], rb[2];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    u32x4_t ra[4], rb[4];
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ra[h] = aval[h] ? *(const uint4*)(arow[h] + lc) : z4;
-      rb[h] = *(const uint4*)(brow[h] + lc);
+    // loads are unconditional (rows past the count read a valid row) and masked when they
+    // are stored to LDS: a conditional load would make the compiler wait for it at once
+    for (int h = 0; h < 4; ++h) {
+      ra[h] = *(const u32x4_t*)(arow[h] + lc);
+      rb[h] = *(const u32x4_t*)(brow[h] + lc);
     }
     for (int k0 = 0; k0 < H; k0 += BK) {
       __syncthreads();  // the previous stage's MFMAs are done with the LDS tiles
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        *(uint4*)(As + (lr + 64 * h) * LDK + lc) = ra[h];
-        *(uint4*)(Bs + (lr + 64 * h) * LDK + lc) = rb[h];
+      for (int h = 0; h < 4; ++h) {
+        *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = aval[h] ? ra[h] : z4;
+        *(u32x4_t*)(Bs + (lr + 32 * h) * LDK + lc) = rb[h];
       }
       __syncthreads();
-      if (k0 + BK < H) {  // next stage's loads overlap this stage's MFMAs
+      const int kn = k0 + BK < H ? k0 + BK : k0;  // last stage: harmless reload
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          ra[h] = aval[h] ? *(const uint4*)(arow[h] + k0 + BK + lc) : z4;
-          rb[h] = *(const uint4*)(brow[h] + k0 + BK + lc);
-        }
+      for (int h = 0; h < 4; ++h) {  // next stage's loads overlap this stage's MFMAs
+        ra[h] = *(const u32x4_t*)(arow[h] + kn + lc);
+        rb[h] = *(const u32x4_t*)(brow[h] + kn + lc);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
         const int ko = kk + 8 * (lane >> 5);
@@ -221,12 +236,12 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
       for (int q = 0; q < 16; ++q) {
         const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
         if (r < en.rows) {
-          const float w = en.shared ? 1.0f : a.v.row_w[en.row0 + r];
-          const float val = pf_silu(acc[rr][0][q]) * acc[rr][1][q] * w;
+          const float val = pf_silu(acc[rr][0][q]) * acc[rr][1][q] * s_w[r - m0];
           act[(size_t)(en.row0 + r) * I + i] = pf_bf16(val);
         }
       }
     }
+    __syncthreads();  // s_w is rewritten by the next tile
   }
 }
 
@@ -243,20 +258,22 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
   const int n = pf_tile_prefix(a, s_mt, first);
   const int NT = H / DBN;
   const int ntiles = s_mt[n] * NT;
-  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 8;     // A: rows lr, lr + 64
-  const int bk = threadIdx.x >> 4, bc = (threadIdx.x & 15) * 8;    // B: k rows bk, bk + 16
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;     // A: rows lr + 32 h
+  // B: this thread's 4 consecutive contraction rows bk .. bk + 3, columns bc .. bc + 8, so the
+  // transpose into LDS is 8 stores of 4 contraction values (8 bytes) each
+  const int bk = (threadIdx.x >> 4) * 4, bc = (threadIdx.x & 15) * 8;
+  for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
     const PfEntry en = pf_entry(a, first + j);
     const int m0 = (mt - s_mt[j]) * BM;
     const int n0 = nt * DBN;
     const uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
-    const uint16_t* arow[2];
-    bool aval[2];
+    const uint16_t* arow[4];
+    bool aval[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = m0 + lr + 64 * h;
+    for (int h = 0; h < 4; ++h) {
+      const int r = m0 + lr + 32 * h;
       aval[h] = r < en.rows;
       arow[h] = act + (size_t)(en.row0 + (aval[h] ? r : 0)) * I;
     }
@@ -268,35 +285,36 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[rr][cc][q] = 0.f;
-    uint4 ra[2], rb[2];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    u32x4_t ra[4], rb[4];
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ra[h] = aval[h] ? *(const uint4*)(arow[h] + lc) : z4;
-      rb[h] = *(const uint4*)(wdt + (size_t)(bk + 16 * h) * H + n0 + bc);
+    for (int h = 0; h < 4; ++h) {
+      ra[h] = *(const u32x4_t*)(arow[h] + lc);
+      rb[h] = *(const u32x4_t*)(wdt + (size_t)(bk + h) * H + n0 + bc);
     }
     for (int k0 = 0; k0 < I; k0 += BK) {
       __syncthreads();
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        *(uint4*)(As + (lr + 64 * h) * LDK + lc) = ra[h];
-        // transpose: 8 consecutive columns of contraction row k go to 8 LDS rows
-        const int k = bk + 16 * h;
-        const uint32_t w[4] = {rb[h].x, rb[h].y, rb[h].z, rb[h].w};
+      for (int h = 0; h < 4; ++h) {
+        *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = aval[h] ? ra[h] : z4;
+      }
+      // transpose the 4 x 8 block: column c gets (row0, row1) and (row2, row3) packed pairs
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          Bs[(bc + 2 * q) * LDK + k] = (uint16_t)(w[q] & 0xffffu);
-          Bs[(bc + 2 * q + 1) * LDK + k] = (uint16_t)(w[q] >> 16);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a0 = rb[0][q], a1 = rb[1][q], a2 = rb[2][q], a3 = rb[3][q];
+        const uint32_t lo01 = (a0 & 0xffffu) | (a1 << 16), hi01 = (a0 >> 16) | (a1 & 0xffff0000u);
+        const uint32_t lo23 = (a2 & 0xffffu) | (a3 << 16), hi23 = (a2 >> 16) | (a3 & 0xffff0000u);
+        *(uint2*)(Bs + (bc + 2 * q) * LDK + bk) = make_uint2(lo01, lo23);
+        *(uint2*)(Bs + (bc + 2 * q + 1) * LDK + bk) = make_uint2(hi01, hi23);
       }
       __syncthreads();
-      if (k0 + BK < I) {
+      const int kn = k0 + BK < I ? k0 + BK : k0;  // last stage: harmless reload
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          ra[h] = aval[h] ? *(const uint4*)(arow[h] + k0 + BK + lc) : z4;
-          rb[h] = *(const uint4*)(wdt + (size_t)(k0 + BK + bk + 16 * h) * H + n0 + bc);
-        }
+      for (int h = 0; h < 4; ++h) {
+        ra[h] = *(const u32x4_t*)(arow[h] + kn + lc);
+        rb[h] = *(const u32x4_t*)(wdt + (size_t)(kn + bk + h) * H + n0 + bc);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
         const int ko = kk + 8 * (lane >> 5);
@@ -350,7 +368,7 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_combine_kernel(PfArgs a) {
   a.y[(size_t)t * H + c] = f32_to_bf16_rne(s);
 }
 
-constexpr int kPfGrid = 1024;  // persistent workgroups per GEMM launch (4 per CU)
+constexpr int kPfGrid = 768;  // persistent workgroups per GEMM launch (3 per CU: 40 KiB LDS each)
 
 // stage 0: gate/up; stage 1: down; stage 2: combine.  e0/e1 (nullable) time the launch.
 hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const void* arena,

@@ -7,8 +7,8 @@
 //
 // Gfx950 design, three launches:
 //   router/top-k  - a workgroup owns 64 tokens: their router logits (fp64 accumulation of
-//                   exact bf16 x bf16 products, operands staged through LDS in 32-wide
-//                   contraction chunks) stay in LDS; one lane per token keeps its top-k
+//                   exact bf16 x bf16 products, operands staged through LDS in 64-wide
+//                   contraction chunks, the next chunk's loads in flight) stay in LDS; one lane per token keeps its top-k
 //                   list (ties to the lower expert id) and the renormalised softmax
 //                   weights; an LDS bitmask per expert gives each (token, choice) its rank
 //                   among the block's tokens routed to the same expert, and the block's
@@ -22,8 +22,8 @@
 namespace moe {
 
 constexpr int PTOK = 64;        // tokens per router workgroup (one wave of top-k lanes)
-constexpr int PKC = 32;         // contraction chunk staged in LDS
-constexpr int PKP = PKC + 2;    // padded LDS row, bf16 elements (17 words: no bank conflicts)
+constexpr int PKC = 64;         // contraction chunk staged in LDS
+constexpr int PKP = PKC + 2;    // padded LDS row, bf16 elements (33 words: no bank conflicts)
 constexpr int kMaxTopK = 16;
 
 struct PrefRouteArgs {
@@ -44,75 +44,101 @@ size_t prefill_router_lds_bytes(const Dims& d) {
   return stage > logits ? stage : logits;
 }
 
-// EPT experts per thread: experts tx, tx + 16, ... (E <= 16 * EPT).
+// EPT experts per thread: experts tx, tx + 16, ... (E <= 16 * EPT); two tokens per thread, so
+// eight waves share a 64-token block (two per SIMD).
+constexpr int PRT = 512;  // threads of the router workgroup
+
 template <int EPT>
-__global__ __launch_bounds__(RT) void prefill_router_topk_kernel(PrefRouteArgs a) {
+__global__ __launch_bounds__(PRT) void prefill_router_topk_kernel(PrefRouteArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Dims& d = a.d;
   const Dev& v = a.v;
   const int E = d.E, H = d.H, K = d.K, T = a.T;
   const int t0 = blockIdx.x * PTOK;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // ty: tokens 2 ty, 2 ty + 1
   __shared__ unsigned long long s_mask[16 * EPT];  // bit t: token t0 + t chose the expert
-  for (int e = threadIdx.x; e < 16 * EPT; e += RT) s_mask[e] = 0ull;
+  for (int e = threadIdx.x; e < 16 * EPT; e += PRT) s_mask[e] = 0ull;
 
   uint16_t* xs = (uint16_t*)smem;   // [PTOK][PKP]
   uint16_t* ws = xs + PTOK * PKP;   // [16 * EPT][PKP]
-  double acc[4][EPT];
+  double acc[2][EPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[i][j] = 0.0;
 
-  for (int k0 = 0; k0 < H; k0 += PKC) {
-    {  // activations: 64 rows x 32 -> one 16-byte chunk per thread
-      const int r = threadIdx.x >> 2, c = (threadIdx.x & 3) * 8;
-      uint4 q = make_uint4(0, 0, 0, 0);
-      if (t0 + r < T) q = *(const uint4*)(a.x + (size_t)(t0 + r) * H + k0 + c);
-      uint32_t* dst = (uint32_t*)(xs + r * PKP + c);
-      dst[0] = q.x; dst[1] = q.y; dst[2] = q.z; dst[3] = q.w;
+  // this thread's 16-byte chunks of a stage: activation row xr (a row past T reads row 0
+  // and is zeroed when stored) and router rows xr + 64 q (q < WQ)
+  constexpr int WQ = (16 * EPT * 8 + PRT - 1) / PRT;  // router chunks per thread
+  const int xr = threadIdx.x >> 3, xc = (threadIdx.x & 7) * 8;
+  const bool xval = t0 + xr < T;
+  const uint16_t* xrow = a.x + (size_t)(xval ? t0 + xr : 0) * H + xc;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  u32x4 rx, rw[WQ];
+  auto load_stage = [&](int k0) {
+    rx = *(const u32x4*)(xrow + k0);
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
+      const int r = xr + 64 * q;
+      rw[q] = r < E ? *(const u32x4*)(a.wr + (size_t)r * H + k0 + xc) : z4;
     }
-    for (int i = threadIdx.x; i < E * 4; i += RT) {  // router rows
-      const int r = i >> 2, c = (i & 3) * 8;
-      const uint4 q = *(const uint4*)(a.wr + (size_t)r * H + k0 + c);
-      uint32_t* dst = (uint32_t*)(ws + r * PKP + c);
-      dst[0] = q.x; dst[1] = q.y; dst[2] = q.z; dst[3] = q.w;
+  };
+  load_stage(0);
+  for (int k0 = 0; k0 < H; k0 += PKC) {
+    __syncthreads();  // the previous stage's reads of the LDS tiles are done
+    {
+      const u32x4 q = xval ? rx : z4;
+      uint32_t* dst = (uint32_t*)(xs + xr * PKP + xc);
+      dst[0] = q[0]; dst[1] = q[1]; dst[2] = q[2]; dst[3] = q[3];
+    }
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
+      const int r = xr + 64 * q;
+      if (r < 16 * EPT) {
+        uint32_t* dst = (uint32_t*)(ws + r * PKP + xc);
+        dst[0] = rw[q][0]; dst[1] = rw[q][1]; dst[2] = rw[q][2]; dst[3] = rw[q][3];
+      }
     }
     __syncthreads();
+    load_stage(k0 + PKC < H ? k0 + PKC : k0);  // the next stage's loads overlap the FMAs
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 4
     for (int kk = 0; kk < PKC; kk += 2) {
-      float xa[4], xb[4];
+      double xa[2], xb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w2 = *(const uint32_t*)(xs + (ty * 4 + i) * PKP + kk);
-        xa[i] = bf16_lo(w2);
-        xb[i] = bf16_hi(w2);
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t w2 = *(const uint32_t*)(xs + (ty * 2 + i) * PKP + kk);
+        xa[i] = (double)bf16_lo(w2);
+        xb[i] = (double)bf16_hi(w2);
       }
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
         const int e = tx + 16 * j;
         if (e < E) {
           const uint32_t w2 = *(const uint32_t*)(ws + e * PKP + kk);
-          const float wa = bf16_lo(w2), wb = bf16_hi(w2);
+          const double wa = (double)bf16_lo(w2), wb = (double)bf16_hi(w2);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)  // bf16 x bf16 products are exact in fp32
-            acc[i][j] += (double)(xa[i] * wa) + (double)(xb[i] * wb);
+          for (int i = 0; i < 2; ++i) {  // the product is exact in fp64: one rounding per add
+            acc[i][j] = __builtin_fma(xa[i], wa, acc[i][j]);
+            acc[i][j] = __builtin_fma(xb[i], wb, acc[i][j]);
+          }
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // logits tile in LDS (the staging area is free after the last barrier); NaN ranks as -inf
   double* sz = (double*)smem;  // [PTOK][E + 1]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = tx + 16 * j;
       if (e < E) {
         const double z = acc[i][j];
-        sz[(ty * 4 + i) * (E + 1) + e] = (z == z) ? z : -__builtin_huge_val();
+        sz[(ty * 2 + i) * (E + 1) + e] = (z == z) ? z : -__builtin_huge_val();
       }
     }
   __syncthreads();
@@ -167,7 +193,7 @@ __global__ __launch_bounds__(RT) void prefill_router_topk_kernel(PrefRouteArgs a
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += RT)
+  for (int e = threadIdx.x; e < E; e += PRT)
     v.blk_cnt[(size_t)blockIdx.x * E + e] = __popcll(s_mask[e]);
   if (live) {
     const unsigned long long below = t == 0 ? 0ull : (~0ull >> (64 - t));
@@ -248,7 +274,7 @@ static hipError_t launch_router(const PrefRouteArgs& a, hipStream_t s, hipEvent_
   const size_t lds = prefill_router_lds_bytes(a.d);
   hipError_t e = set_lds(prefill_router_topk_kernel<EPT>, lds);
   if (e != hipSuccess) return e;
-  return launch_timed(prefill_router_topk_kernel<EPT>, dim3((a.T + PTOK - 1) / PTOK), dim3(RT),
+  return launch_timed(prefill_router_topk_kernel<EPT>, dim3((a.T + PTOK - 1) / PTOK), dim3(PRT),
                       lds, s, e0, nullptr, a);
 }
 
