@@ -90,7 +90,58 @@ def cpu_baseline(wb, tokens: int) -> dict:
             "kind": "oracle",
             "sample": f"first {tokens} token step(s) x {wl.layers} layers of the same workload, "
                       f"full float64 route+top-k+dedup+LRU+SwiGLU FFN, {dt:.1f} s",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+            "seconds": dt, "host_cpus": os.cpu_count(),
+            "lru_only_steps_per_s": _lru_only_rate(wb)}
+
+
+def _lru_only_rate(wb, tokens: int = 64) -> float:
+    """The oracle's LRU rule alone, single-threaded, in layer steps per second: the distinct
+    expert sets of the first `tokens` token steps are routed by the oracle first (untimed),
+    then replayed through a cold cache of the workload's size."""
+    from oracle.dedup import dedup
+    from oracle.formats import bf16_to_f64
+    from oracle.lru import LRUCache
+    from oracle.router import router_logits, topk_softmax
+    wl = wb.wl
+    tokens = min(tokens, wb.acts_np.shape[0])
+    sets = []
+    for t in range(tokens):
+        for l in range(wl.layers):
+            x = bf16_to_f64(wb.acts_np[t, l]).reshape(-1, wl.hidden)
+            idx, _ = topk_softmax(router_logits(x, bf16_to_f64(wb.router_np[l])), wl.top_k)
+            sets.append((l, dedup(idx, wl.experts)[0]))
+    cache = LRUCache(wl.capacity, wl.n_keys)
+    t0 = time.perf_counter()
+    for s, (l, U) in enumerate(sets):
+        cache.step(l, U, wl.experts, s)
+    return round(len(sets) / (time.perf_counter() - t0), 1)
+
+
+def hbm_stream_probe(dev) -> dict:
+    """Measured device-memory streaming rates on this GPU (reference for the HBM roofline):
+    a 4 GiB device-to-device copy (read + write bytes) and a 4 GiB sum (read bytes)."""
+    import torch
+    n = 1 << 32
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    copy = 2 * n * 5 / (time.perf_counter() - t0) / 1e9
+    f = a.view(torch.float32)
+    f.sum()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        f.sum()
+    torch.cuda.synchronize()
+    read = n * 5 / (time.perf_counter() - t0) / 1e9
+    del a, b, f
+    return {"copy_GBps": round(copy, 1), "read_GBps": round(read, 1), "bytes": n}
 
 
 def _with_cache_frac(wl, frac: float):
@@ -279,6 +330,8 @@ def main() -> None:
         wl = wl.with_layers(args.layers)
     if args.cache_frac > 0:
         wl = _with_cache_frac(wl, args.cache_frac)
+    if wl.resize_at >= 0 and not args.steps_given:
+        args.steps = wl.token_steps - args.warmup  # run through the resize to the end
     n_tok = args.warmup + args.steps
     n_all = n_tok + args.breakdown_steps
     if wl.kind != "decode":
@@ -289,32 +342,54 @@ def main() -> None:
           f"I={wl.inter} fmt={wl.fmt} C={wl.capacity} pool={wl.pool_bytes / 1e9:.2f} GB",
           file=sys.stderr, flush=True)
     t_setup = time.perf_counter()
-    wb = Workbench(wl, groups=args.groups, max_capacity=wl.capacity)
+    wb = Workbench(wl, groups=args.groups)
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
     L = wl.layers
-    for t in range(args.warmup):
+    resize_at = wl.resize_at if 0 <= wl.resize_at < n_tok else -1
+
+    def token(t):
         for l in range(L):
             wb.step(t, l)
+
+    for t in range(args.warmup):
+        if t == resize_at:
+            wb.sync()
+            wb.resize(wl.resize_capacity)
+        token(t)
     wb.sync()
     st0 = wb.stats()
     if not args.no_profile:
         moe_profile_enable(wb.handle, PROF_GATE_UP, args.profile_every)
+    # the timed tokens in windows (their rates give median / min / max); a cache resize at a
+    # safe point inside the timed region is timed on its own and counted in the total
+    n_win = 5
+    bounds = [args.warmup + (args.steps * i) // n_win for i in range(n_win + 1)]
+    segments, resize_s = [], None  # (tokens, seconds, "before" | "after" the resize)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.warmup, n_tok):
-        for l in range(L):
-            wb.step(t, l)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
+    for w in range(n_win):
+        t, t_end = bounds[w], bounds[w + 1]
+        while t < t_end:
+            if t == resize_at:
+                r0 = time.perf_counter()
+                wb.resize(wl.resize_capacity)
+                torch.cuda.synchronize()
+                resize_s = time.perf_counter() - r0
+            stop = resize_at if t < resize_at < t_end else t_end
+            t0 = time.perf_counter()
+            for tt in range(t, stop):
+                token(tt)
+            torch.cuda.synchronize()
+            segments.append((stop - t, time.perf_counter() - t0,
+                             "after" if 0 <= resize_at <= t else "before"))
+            t = stop
+    wall = sum(dt for _, dt, _ in segments) + (resize_s or 0.0)
     prof = moe_profile_read(wb.handle) if not args.no_profile else None
     st1 = wb.stats()
     brk = None
     if not args.no_profile and args.breakdown_steps > 0:
         moe_profile_enable(wb.handle, PROF_ALL)
         for t in range(n_tok, n_all):
-            for l in range(L):
-                wb.step(t, l)
+            token(t)
         brk = moe_profile_read(wb.handle)
         moe_profile_enable(wb.handle, 0)
     hits = st1["hits"] - st0["hits"]
@@ -364,6 +439,22 @@ def main() -> None:
             "gate_up_ms_per_token": round(brk["gate_up"]["ms"] / nb, 3),
             "down_ms_per_token": round(brk["down"]["ms"] / nb, 3)}
     fill["link_frac_of_memcpy"] = round(fill["link_GBps"] / h2d["blob_GBps"], 3)
+    T = wl.tokens_per_step
+    rates = sorted(n * T / dt for n, dt, _ in segments if n > 0)
+    extra["repeats"] = {"windows": len(rates), "tok_s": [round(r, 3) for r in rates],
+                        "median": round(rates[len(rates) // 2], 3), "min": round(rates[0], 3),
+                        "max": round(rates[-1], 3)}
+    if resize_s is not None:
+        side = {k: (sum(n for n, _, sd in segments if sd == k),
+                    sum(dt for _, dt, sd in segments if sd == k)) for k in ("before", "after")}
+        extra["resize"] = {
+            "at_token_step": resize_at, "from_slots": wl.capacity,
+            "to_slots": wl.resize_capacity, "latency_ms": round(resize_s * 1e3, 3),
+            "tok_s_before": round(side["before"][0] * T / side["before"][1], 3)
+            if side["before"][1] > 0 else None,
+            "tok_s_after": round(side["after"][0] * T / side["after"][1], 3)
+            if side["after"][1] > 0 else None}
+    extra["hbm_stream"] = hbm_stream_probe(wb.dev)
 
     cpu = None
     if not args.no_cpu_baseline:
