@@ -71,6 +71,16 @@ def h2d_memcpy_probe(pool_addr: int, pool_bytes: int, blob: int, dev_buf_ptr: in
     return out
 
 
+def _host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wb, tokens: int) -> dict:
     """The float64 oracle as it stands, on the first `tokens` token steps of the workload."""
     from threadpoolctl import threadpool_info
@@ -90,7 +100,7 @@ def cpu_baseline(wb, tokens: int) -> dict:
             "kind": "oracle",
             "sample": f"first {tokens} token step(s) x {wl.layers} layers of the same workload, "
                       f"full float64 route+top-k+dedup+LRU+SwiGLU FFN, {dt:.1f} s",
-            "seconds": dt, "host_cpus": os.cpu_count(),
+            "seconds": dt, "host_cpus": os.cpu_count(), "host_cpu_model": _host_cpu_model(),
             "lru_only_steps_per_s": _lru_only_rate(wb)}
 
 
@@ -195,7 +205,7 @@ def cpu_baseline_prefill(wb, tokens: int) -> dict:
             "sample": f"first {tokens} tokens of the chunk through layer 0 (full float64 route, "
                       f"top-k, dedup, LRU, SwiGLU FFN), {dt:.1f} s, scaled to "
                       f"{wb.wl.layers} layers",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+            "seconds": dt, "host_cpus": os.cpu_count(), "host_cpu_model": _host_cpu_model()}
 
 
 def run_prefill(args, wl) -> None:
@@ -209,7 +219,7 @@ def run_prefill(args, wl) -> None:
     from expert_cache_offload_amd.runner import Workbench
 
     groups = args.groups if args.groups > 0 else 16
-    steps = args.steps if args.steps_given else 2
+    steps = args.steps if args.steps_given else 5
     warmup = args.warmup if args.warmup_given else 1
     T, L, H, I, K = wl.tokens_per_step, wl.layers, wl.hidden, wl.inter, wl.top_k
     print(f"[bench] prefill {wl.name}: L={L} T={T} H={H} E={wl.experts} k={K} I={I} "
@@ -287,8 +297,14 @@ def run_prefill(args, wl) -> None:
                  "kernel_GBps": round(fill_bytes / fk_s / 1e9, 2) if fk_s > 0 else None,
                  "h2d_memcpy_blob_GBps": round(h2d["blob_GBps"], 2),
                  "h2d_memcpy_1GiB_GBps": round(h2d["large_GBps"], 2)},
-        "ablation": {"double_buffered_s": round(min(times), 4), "serial_s": round(serial, 4),
-                     "serial_over_double_buffered": round(serial / min(times), 4)},
+        "ablation": {"double_buffered_s": round(sorted(times)[len(times) // 2], 4),
+                     "serial_s": round(serial, 4),
+                     "serial_over_double_buffered":
+                         round(serial / sorted(times)[len(times) // 2], 4)},
+        "repeats": {"chunks": len(times),
+                    "tok_s": [round(T / t, 1) for t in sorted(times, reverse=True)],
+                    "median": round(T / sorted(times)[len(times) // 2], 1),
+                    "min": round(T / max(times), 1), "max": round(T / min(times), 1)},
     }
     print(json.dumps(line), flush=True)
 
@@ -455,6 +471,9 @@ def main() -> None:
             "tok_s_after": round(side["after"][0] * T / side["after"][1], 3)
             if side["after"][1] > 0 else None}
     extra["hbm_stream"] = hbm_stream_probe(wb.dev)
+    if roofline is not None:
+        roofline["frac_of_measured_read"] = round(
+            roofline["achieved"] / extra["hbm_stream"]["read_GBps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:

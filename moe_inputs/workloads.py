@@ -9,6 +9,8 @@ Each workload is one model shape plus a cache budget and a token schedule:
   tokens at batch 1.
 * ``qwen35b_prefill`` - the same shape, one 16,384-token prefill chunk with
   i.i.d. N(0,1) activations, cache 30% of the pool.
+* ``qwen35b_decode_b8`` - the 35B shape with 8 concurrent decode streams batched (8 tokens per
+  layer step, one cache step and one dedup for all of them).
 * ``dsv4_fp8_decode`` - 43 layers, hidden 4096, 256 routed experts top-8 plus one
   GPU-resident shared expert, intermediate 2048, fp8-e4m3 with a fp32 scale per
   1x128 block (24.75 MiB per expert), cache = 17% of the pool, 512 decode tokens.
@@ -98,6 +100,8 @@ WORKLOADS = {
     "qwen35b_decode": Workload("qwen35b_decode", 48, 2048, 128, 8, 768, 0, 0.30, 1, 512, "decode"),
     "qwen35b_prefill": Workload("qwen35b_prefill", 48, 2048, 128, 8, 768, 0, 0.30, 16384, 1,
                                 "prefill"),
+    "qwen35b_decode_b8": Workload("qwen35b_decode_b8", 48, 2048, 128, 8, 768, 0, 0.30, 8, 512,
+                                  "decode"),
     "dsv4_fp8_decode": Workload("dsv4_fp8_decode", 43, 4096, 256, 8, 2048, 1, 0.17, 1, 512,
                                 "decode", has_shared=True),
     "glm_mxfp4_4stream": Workload("glm_mxfp4_4stream", 8, 6144, 256, 8, 2048, 2, 0.40, 4, 1024,

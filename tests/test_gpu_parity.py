@@ -94,6 +94,17 @@ def test_bf16_decode_multilayer_evictions(groups):
     _log(f"bf16 4-layer: max rel-L2 {max(errs):.2e}")
 
 
+@pytest.mark.parametrize("groups", [0, 3])
+def test_bf16_decode_eight_streams(groups):
+    """8 decode streams batched at the 35B shape: one dedup and one cache step for 8 tokens,
+    experts shared by several tokens read once."""
+    wl = mi.WORKLOADS["qwen35b_decode_b8"].with_layers(3).with_steps(10)
+    _log(f"case {wl.name} groups={groups} C={wl.capacity}")
+    with _bench(wl, groups=groups) as wb:
+        errs = run_parity(wb, wl.token_steps, ffn_every=4)
+    _log(f"bf16 8 streams: max rel-L2 {max(errs):.2e}")
+
+
 @pytest.mark.parametrize("groups", [0, 2])
 def test_fp8_decode_with_shared_expert(groups):
     """284B-like shape: H 4096, 256 experts top-8 + shared expert, fp8 e4m3 1x128 blocks."""
