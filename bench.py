@@ -372,6 +372,9 @@ def main() -> None:
             wb.sync()
             wb.resize(wl.resize_capacity)
         token(t)
+        if t % 16 == 15:
+            wb.sync()
+            print(f"[bench] warmup token {t}", file=sys.stderr, flush=True)
     wb.sync()
     st0 = wb.stats()
     if not args.no_profile:
@@ -397,6 +400,8 @@ def main() -> None:
             torch.cuda.synchronize()
             segments.append((stop - t, time.perf_counter() - t0,
                              "after" if 0 <= resize_at <= t else "before"))
+            print(f"[bench] tokens {t}..{stop - 1}: {(stop - t) * wl.tokens_per_step / segments[-1][1]:.2f} "
+                  "tok/s", file=sys.stderr, flush=True)
             t = stop
     wall = sum(dt for _, dt, _ in segments) + (resize_s or 0.0)
     prof = moe_profile_read(wb.handle) if not args.no_profile else None
