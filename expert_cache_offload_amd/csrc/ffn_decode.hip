@@ -179,6 +179,18 @@ __device__ __forceinline__ int n_entries_in_launch(const FfnArgs& a, int nHit, i
 
 __device__ __forceinline__ bool resolve(const FfnArgs& a, int j, Entry& en) {
   const Dev& v = a.v;
+  if (a.sel == 2 && !a.d.has_shared) {
+    // every entry of the step, no shared expert: entry j is table row j, so its load goes
+    // out together with the header's (rows past the step's count are never used)
+    const int4 e = v.ent[j < a.d.umax ? j : 0];
+    if (j >= v.hdr[HDR_NHIT] + v.hdr[HDR_NMISS]) return false;
+    en.g = j;
+    en.shared = false;
+    en.ntok = e.y;
+    en.row0 = e.z;
+    en.blob = a.arena + (size_t)e.x * (size_t)a.d.S;
+    return true;
+  }
   const int nHit = v.hdr[HDR_NHIT], nMiss = v.hdr[HDR_NMISS];
   int first;
   const int n = n_entries_in_launch(a, nHit, nMiss, first);

@@ -58,6 +58,29 @@ def test_prefill_tiny_shape_with_shared_expert():
         _log(f"tiny prefill groups={groups}: max rel-L2 {max(errs):.2e}")
 
 
+@pytest.mark.parametrize("tokens", [9, 64, 65, 130])
+def test_prefill_block_edges(tokens):
+    """The smallest many-token step (9), exactly one 64-token block, one past it, and two
+    blocks plus two tokens, at the tiny shape over two layers (16 slots: the second layer
+    evicts)."""
+    base = dataclasses.replace(mi.WORKLOADS["tiny"], layers=2, fixed_capacity=16)
+    wl = base.as_prefill(tokens)
+    _log(f"case {wl.name}")
+    with _bench(wl, groups=0) as wb:
+        _run_chunk(wb)
+
+
+def test_prefill_256_experts():
+    """256 experts top-8 (16 experts per router thread), hidden 1024, intermediate 512, bf16,
+    200 tokens over two layers with 300 slots."""
+    wl = mi.Workload("e256_bf16", 2, 1024, 256, 8, 512, 0, 0.0, 200, 1, "prefill",
+                     fixed_capacity=300)
+    _log(f"case {wl.name} C={wl.capacity}")
+    with _bench(wl, groups=2) as wb:
+        errs = _run_chunk(wb)
+    _log(f"256 experts: max rel-L2 {max(errs):.2e}")
+
+
 @pytest.mark.parametrize("groups", [0, 4])
 def test_prefill_qwen_shape_ragged_chunk(groups):
     """35B-A3B expert shape, 4 layers, a 300-token chunk (4 full blocks and a ragged one):
