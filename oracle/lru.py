@@ -27,6 +27,13 @@ R5  miss i takes free slot n + i while free slots last, then the slots of the
 R6  victims leave; every key of U (hits and misses) moves to the MRU end in
     ascending expert id with stamp = s, the global step counter.  The list order
     is therefore always ascending (stamp, key).
+R8  prefetch (steps of many tokens only): before layer l' is routed, a prefetch step of
+    layer l' is an R1-R6 step whose U is every expert of l', except that the victims also
+    skip the keys of a protected set (the distinct keys of the layer step just before it,
+    whose expert FFN may still be reading their slots).  It takes its own value of the
+    step counter.  (FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理, on the prefill union:
+    a long prefill routes to nearly every expert of every layer, so layer l' can be
+    fetched while layer l computes.)
 R7  resize to C': if n <= C' nothing moves.  Otherwise the C' keys nearest the
     MRU end survive; holes in [0, C') are filled, in ascending slot order, by the
     survivors that sit in slots >= C', taken in ascending old-slot order; stamps
@@ -69,7 +76,8 @@ class LRUCache:
     def slot_of(self, key: int) -> int:
         return self.order.get(key, -1)
 
-    def step(self, layer: int, U, E: int, s: int) -> StepRecord:
+    def step(self, layer: int, U, E: int, s: int, protected=()) -> StepRecord:
+        """R1-R6; `protected` keys are never victims either (R8)."""
         keys = [layer * E + int(e) for e in U]                          # R1 (U ascending)
         if len(keys) > self.C:
             raise CapacityError(f"{len(keys)} distinct experts exceed capacity {self.C}")
@@ -77,7 +85,7 @@ class LRUCache:
         misses = [key for key, h in zip(keys, hit) if not h]             # R3
         n_free = self.C - self.n
         need = max(0, len(misses) - n_free)                              # R4
-        in_step = set(keys)
+        in_step = set(keys) | set(protected)
         victims = []
         for key in self.order:
             if len(victims) == need:

@@ -8,6 +8,8 @@ byte copy of pool[key] into the slot, so the FFN reads the pool blob directly.
 
 Step counter: s increments once per layer step; decode visits token step t
 outer and layer l inner (s = t * L + l); a prefill chunk visits layers in order.
+With prefetch (R8), a prefetch step of layer l + 1 follows the step of layer l and takes
+the next counter value.
 At decode all streams of a step (T tokens) share one dedup and one cache step.
 The resize happens at the safe point before token step ``resize_at``.
 """
@@ -88,6 +90,15 @@ class Oracle:
         out = LayerStep(token_step, layer, self.s, idx, w, U, count, offset, perm, rec, y)
         self.s += 1
         return out
+
+    def prefetch(self, layer: int, protected_layer: int, protected_U) -> StepRecord:
+        """R8: fetch every expert of `layer` before it is routed; the keys of the previous
+        layer step (`protected_layer`, its distinct experts `protected_U`) are not evicted."""
+        E = self.wl.experts
+        prot = [protected_layer * E + int(e) for e in protected_U]
+        rec = self.cache.step(layer, list(range(E)), E, self.s, protected=prot)
+        self.s += 1
+        return rec
 
     def resize(self, new_capacity: int):
         return self.cache.resize(new_capacity)

@@ -208,3 +208,91 @@ def test_prefill_full_capacity_case():
     assert r.misses[:51] == [(14 * E + e, 14 * E + e, -1) for e in range(51)]
     assert r.misses[51:] == [(14 * E + 51 + i, i, i) for i in range(77)]
     assert r.n == C
+
+
+def _brute_force_protected(seq, C, E):
+    """Independent model of R1-R6 + R8: the cache is a dict key -> (stamp, slot); victims are
+    the `need` smallest (stamp, key) outside U and the protected keys."""
+    cache = {}
+    free = list(range(C))
+    out = []
+    for s, (l, U, prot) in enumerate(seq):
+        keys = [l * E + e for e in U]
+        hit = [k in cache for k in keys]
+        misses = [k for k, h in zip(keys, hit) if not h]
+        n_free = len(free)
+        need = max(0, len(misses) - n_free)
+        skip = set(keys) | set(prot)
+        cand = sorted((st, k) for k, (st, sl) in cache.items() if k not in skip)
+        victims = [k for _, k in cand[:need]]
+        assert len(victims) == need
+        assigned = []
+        free_sorted = sorted(free)
+        for i, k in enumerate(misses):
+            if i < n_free:
+                assigned.append((k, free_sorted[i], -1))
+            else:
+                v = victims[i - n_free]
+                assigned.append((k, cache[v][1], v))
+        for v in victims:
+            del cache[v]
+        for k, sl, _ in assigned:
+            if sl in free:
+                free.remove(sl)
+            cache[k] = (s, sl)
+        for k in keys:
+            cache[k] = (s, cache[k][1])
+        out.append((hit, assigned, {k: sl for k, (st, sl) in cache.items()}))
+    return out
+
+
+def test_prefetch_steps_against_brute_force():
+    """R8: route steps alternating with prefetch steps of the next layer (every expert, the
+    previous step's keys protected) against an independent dictionary model."""
+    L, E = 4, 6
+    for seed in range(5):
+        rng = np.random.default_rng(100 + seed)
+        for C in (2 * E, 2 * E + 3, 3 * E):
+            seq = []
+            prev = None
+            for rep in range(3):
+                for l in range(L):
+                    if prev is not None:
+                        seq.append((l, list(range(E)), [prev[0] * E + e for e in prev[1]]))
+                    U = sorted(set(int(x) for x in rng.integers(0, E, size=4)))
+                    seq.append((l, U, []))
+                    prev = (l, U)
+            c = LRUCache(C, L * E)
+            ref = _brute_force_protected(seq, C, E)
+            for s, (l, U, prot) in enumerate(seq):
+                rec = c.step(l, U, E, s, protected=prot)
+                hit, assigned, content = ref[s]
+                assert rec.hit == hit, (seed, C, s)
+                assert [tuple(m) for m in rec.misses] == assigned, (seed, C, s)
+                got = {k: sl for sl, k in enumerate(rec.key_of) if k >= 0}
+                assert got == content, (seed, C, s)
+                assert not any(v in set(prot) for _, _, v in rec.misses)
+
+
+def test_prefetch_makes_the_next_step_all_hits_and_protects():
+    L, E = 3, 8
+    c = LRUCache(2 * E, L * E)
+    c.step(0, [1, 2, 5], E, 0)
+    pf = c.step(1, list(range(E)), E, 1, protected=[0 * E + e for e in (1, 2, 5)])
+    assert sum(not h for h in pf.hit) == E  # every expert of layer 1 fetched
+    r = c.step(1, [0, 3, 7], E, 2)
+    assert all(r.hit) and not r.misses
+    # the next prefetch must evict the oldest unprotected keys: layer 0's keys go first,
+    # layer 1's routed keys (protected) stay
+    pf2 = c.step(2, list(range(E)), E, 3, protected=[1 * E + e for e in (0, 3, 7)])
+    victims = [v for _, _, v in pf2.misses if v >= 0]
+    assert set(victims).isdisjoint({E + 0, E + 3, E + 7})
+    assert {0 * E + e for e in (1, 2, 5)} <= set(victims)
+
+
+def test_prefetch_capacity_error_when_protected_fill_the_cache():
+    E = 4
+    c = LRUCache(E + 2, 2 * E)
+    c.step(0, [0, 1, 2, 3], E, 0)
+    with pytest.raises(CapacityError):
+        c.step(1, list(range(E)), E, 1, protected=[0, 1, 2, 3])
