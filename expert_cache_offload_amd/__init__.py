@@ -84,6 +84,7 @@ _SIGS = {
     "moe_plan_read": (_i32, [_vp, ctypes.POINTER(MoePlanHost)]),
     "moe_stats": (_i32, [_vp, ctypes.POINTER(MoeCounters)]),
     "moe_profile_enable": (_i32, [_vp, _i32, _i32]),
+    "moe_set_prefetch": (_i32, [_vp, _i32]),
     "moe_profile_read": (_i32, [_vp, ctypes.POINTER(MoeProfile)]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_last_hip_error": (_i32, [_vp]),
@@ -219,6 +220,11 @@ def moe_stats(handle: int) -> dict:
     c = MoeCounters()
     _check(_lib.moe_stats(handle, ctypes.byref(c)), "moe_stats", handle)
     return {"steps": c.steps, "hits": c.hits, "misses": c.misses, "bytes_filled": c.bytes_filled}
+
+
+def moe_set_prefetch(handle: int, enable: bool) -> None:
+    """Prefetch the next layer's experts during steps of many tokens (see the header)."""
+    _check(_lib.moe_set_prefetch(handle, int(bool(enable))), "moe_set_prefetch", handle)
 
 
 def moe_profile_enable(handle: int, mask: int = PROF_ALL, every: int = 1) -> None:

@@ -23,7 +23,8 @@ int decode_ntok(int T);
 int down_columns_per_block(int fmt);
 int down_row_splits(int inter);
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
-                       int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+                       int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                       int prefetch, int E);
 hipError_t launch_init(const Dev& v, int max_capacity, int n_keys, int capacity, hipStream_t s);
 hipError_t launch_resize(const Dev& v, int new_capacity, int max_capacity, int E,
                          const void* old_arena, void* new_arena, long long S, hipStream_t s);
@@ -36,6 +37,7 @@ hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const 
                               const void* shared_blob, void* y, int sel, int group, int ngroups,
                               int T, int stage, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 bool prefill_ffn_supported(const Dims& d);
+hipError_t launch_prefetch_plan(const Dims& d, const Dev& v, int layer, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -54,7 +56,7 @@ struct Layout {
   size_t key_of, stamp, slot_of, ctrl, stats, hdr, U, u_slot, u_hit, hit_list, miss_list,
       miss_key, miss_slot, miss_victim, count, offset, perm, inv_pos, tk_idx, tk_w, logits,
       act, act_shared, yexp, yexp_shared, ent, row_tok, row_w, moves, blk_cnt, blk_off, brank,
-      pact, pact_shared, pyexp, pyexp_shared, total;
+      pact, pact_shared, pyexp, pyexp_shared, pf_hdr, pf_list, pf_ent, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -128,6 +130,9 @@ Layout make_layout(const Dims& d) {
   L.pact_shared = take(d.has_shared ? sizeof(uint16_t) * T * d.I : 0);
   L.pyexp = take(sizeof(float) * A * d.H);
   L.pyexp_shared = take(d.has_shared ? sizeof(float) * T * d.H : 0);
+  L.pf_hdr = take(I4 * HDR_WORDS);
+  L.pf_list = take(I4 * (size_t)(11 * d.E + 1));
+  L.pf_ent = take(sizeof(int) * 4 * (size_t)d.E);
   L.total = o;
   return L;
 }
@@ -171,6 +176,9 @@ Dev make_dev(void* ws, const Layout& L) {
   v.pact_shared = (uint16_t*)(b + L.pact_shared);
   v.pyexp = (float*)(b + L.pyexp);
   v.pyexp_shared = (float*)(b + L.pyexp_shared);
+  v.pf_hdr = (int*)(b + L.pf_hdr);
+  v.pf_list = (int*)(b + L.pf_list);
+  v.pf_ent = (int4*)(b + L.pf_ent);
   return v;
 }
 
@@ -284,6 +292,10 @@ struct moe_cache_s {
   const void* pool_dev;
   hipEvent_t ev_plan;
   hipEvent_t ev_fill[kMaxGroups];
+  int prefetch;                    // prefetch the next layer in steps of many tokens
+  int pf_layer[2] = {-1, -1};      // layer whose prefetch is in flight, by layer parity
+  hipEvent_t ev_pfplan;
+  hipEvent_t ev_pf[2];
   State state;
   int plan_T;
   int plan_layer;
@@ -371,6 +383,9 @@ moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t ma
   hipError_t e = hipEventCreateWithFlags(&c->ev_plan, hipEventDisableTiming);
   for (int g = 0; g < kMaxGroups && e == hipSuccess; ++g)
     e = hipEventCreateWithFlags(&c->ev_fill[g], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_pfplan, hipEventDisableTiming);
+  for (int q = 0; q < 2 && e == hipSuccess; ++q)
+    e = hipEventCreateWithFlags(&c->ev_pf[q], hipEventDisableTiming);
   if (e == hipSuccess)
     e = launch_init(c->v, max_capacity, shape->layers * shape->experts, capacity,
                     (hipStream_t)stream);
@@ -389,6 +404,9 @@ moe_status moe_cache_destroy(moe_cache c) {
   if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
   for (int g = 0; g < kMaxGroups; ++g)
     if (c->ev_fill[g]) (void)hipEventDestroy(c->ev_fill[g]);
+  if (c->ev_pfplan) (void)hipEventDestroy(c->ev_pfplan);
+  for (int q = 0; q < 2; ++q)
+    if (c->ev_pf[q]) (void)hipEventDestroy(c->ev_pf[q]);
   delete c;
   return MOE_OK;
 }
@@ -396,6 +414,7 @@ moe_status moe_cache_destroy(moe_cache c) {
 moe_status moe_cache_resize(moe_cache c, int32_t new_capacity, void* new_arena, void* stream) {
   if (!c) return MOE_E_INVALID;
   if (c->state != State::Idle) return MOE_E_BUSY;
+  if (c->pf_layer[0] >= 0 || c->pf_layer[1] >= 0) return MOE_E_BUSY;  // prefetch in flight
   const int floor_c = c->d.umax;
   if (new_capacity < floor_c || new_capacity > c->max_capacity) return MOE_E_CAPACITY;
   if (new_arena && !aligned16(new_arena)) return MOE_E_INVALID;
@@ -453,6 +472,43 @@ static hipError_t ffn_launch(moe_cache c, const void* x, int T, const void* shar
   });
 }
 
+// Prefetch of every expert of `layer` (steps of many tokens, prefetch mode): its plan on `cs`
+// right after the step plan before it, its fills on `fs` (after the fills already queued
+// there); the FFN of `layer` waits for them.
+static hipError_t issue_prefetch(moe_cache c, int layer, hipStream_t cs, hipStream_t fs) {
+  hipError_t e = launch_prefetch_plan(c->d, c->v, layer, cs);
+  if (e == hipSuccess && fs != cs) {
+    e = hipEventRecord(c->ev_pfplan, cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(fs, c->ev_pfplan, 0);
+  }
+  if (e == hipSuccess)
+    e = c->prof.timed(Profiler::FILL, fs, [&](hipEvent_t e0, hipEvent_t e1) {
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, fs, e0, e1, 1,
+                         c->d.E);
+    });
+  if (e == hipSuccess) e = hipEventRecord(c->ev_pf[layer & 1], fs);
+  if (e == hipSuccess) c->pf_layer[layer & 1] = layer;
+  return e;
+}
+
+static hipError_t wait_prefetch(moe_cache c, int layer, hipStream_t s) {
+  if (c->pf_layer[layer & 1] != layer) return hipSuccess;
+  c->pf_layer[layer & 1] = -1;
+  return hipStreamWaitEvent(s, c->ev_pf[layer & 1], 0);
+}
+
+static bool prefetch_next(moe_cache c, int layer, int T) {
+  return c->prefetch && T > kDecodeMaxTokens && layer + 1 < c->d.L;
+}
+
+moe_status moe_set_prefetch(moe_cache c, int32_t enable) {
+  if (!c || (enable != 0 && enable != 1)) return MOE_E_INVALID;
+  if (enable && c->d.nblk == 0) return MOE_E_INVALID;  // a handle for decode steps only
+  if (c->state != State::Idle || c->pf_layer[0] >= 0 || c->pf_layer[1] >= 0) return MOE_E_BUSY;
+  c->prefetch = enable;
+  return MOE_OK;
+}
+
 moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t T,
                               const void* w_router, int32_t* topk_idx, float* topk_w,
                               void* stream) {
@@ -481,7 +537,7 @@ moe_status moe_fill_misses(moe_cache c, int32_t groups, void* fill_stream) {
   hipError_t e = hipStreamWaitEvent(s, c->ev_plan, 0);
   for (int g = 0; g < groups && e == hipSuccess; ++g) {
     e = c->prof.timed(Profiler::FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s, e0, e1);
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, g, groups, kFillGrid, s, e0, e1, 0, c->d.E);
     });
     if (e == hipSuccess) e = hipEventRecord(c->ev_fill[g], s);
   }
@@ -502,9 +558,9 @@ moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
   auto& P = c->prof;
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
   const int G = c->fill_groups;
-  hipError_t e = hipSuccess;
+  hipError_t e = wait_prefetch(c, layer, s);  // hits may have been prefetched
   (void)P;
-  if (T > 0)  // hit experts and the shared expert: no fill to wait for
+  if (e == hipSuccess && T > 0)  // hit experts and the shared expert: no fill to wait for
     e = ffn_launch(c, x, T, shared_blob, y, 0, 0, 1, nu + c->d.has_shared, 0, s);
   for (int g = 0; g < G && e == hipSuccess; ++g) {
     e = hipStreamWaitEvent(s, c->ev_fill[g], 0);
@@ -521,7 +577,8 @@ moe_status moe_expert_ffn(moe_cache c, int32_t layer, const void* x, int32_t T,
 // joins two queues, so consecutive kernels start back to back.
 static moe_status layer_step_serial(moe_cache c, int32_t layer, const void* x, int32_t T,
                                     const void* w_router, const void* shared_blob,
-                                    int32_t* topk_idx, float* topk_w, void* y, hipStream_t s) {
+                                    int32_t* topk_idx, float* topk_w, void* y, hipStream_t s,
+                                    hipStream_t fs) {
   if (T > 0 && (!aligned16(x) || !aligned16(w_router) || ((uintptr_t)y & 3)))
     return MOE_E_INVALID;
   if (c->d.has_shared && T > 0 && !aligned16(shared_blob)) return MOE_E_INVALID;
@@ -529,9 +586,11 @@ static moe_status layer_step_serial(moe_cache c, int32_t layer, const void* x, i
   hipError_t e = route_launch(c, layer, x, T, w_router, topk_idx, topk_w, s);
   if (e == hipSuccess)
     e = P.timed(Profiler::FILL, s, [&](hipEvent_t e0, hipEvent_t e1) {
-      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, s, e0, e1);
+      return launch_fill(c->v, c->pool_dev, c->arena, c->d.S, 0, 1, kFillGrid, s, e0, e1, 0, c->d.E);
     });
   const int nu = T * c->d.K < c->d.E ? T * c->d.K : c->d.E;
+  if (e == hipSuccess && prefetch_next(c, layer, T)) e = issue_prefetch(c, layer + 1, s, fs);
+  if (e == hipSuccess) e = wait_prefetch(c, layer, s);
   if (e == hipSuccess && T > 0)
     e = ffn_launch(c, x, T, shared_blob, y, 2, 0, 1, nu + c->d.has_shared, 1, s);
   if (e != hipSuccess) return hip_fail(c, e);
@@ -554,11 +613,17 @@ moe_status moe_layer_step(moe_cache c, int32_t layer, const void* x, int32_t T,
   if (T > kDecodeMaxTokens && !many_tokens_ok(c->d)) return MOE_E_INVALID;
   if (groups == 0)
     return layer_step_serial(c, layer, x, T, w_router, shared_blob, topk_idx, topk_w, y,
-                             (hipStream_t)compute_stream);
+                             (hipStream_t)compute_stream,
+                             fill_stream ? (hipStream_t)fill_stream : (hipStream_t)compute_stream);
   moe_status st = moe_route_classify(c, layer, x, T, w_router, topk_idx, topk_w, compute_stream);
   if (st != MOE_OK) return st;
   st = moe_fill_misses(c, groups, fill_stream);
   if (st != MOE_OK) return st;
+  if (prefetch_next(c, layer, T)) {
+    hipError_t e = issue_prefetch(c, layer + 1, (hipStream_t)compute_stream,
+                                  (hipStream_t)fill_stream);
+    if (e != hipSuccess) return hip_fail(c, e);
+  }
   return moe_expert_ffn(c, layer, x, T, shared_blob, y, compute_stream);
 }
 

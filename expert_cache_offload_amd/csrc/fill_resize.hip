@@ -24,10 +24,12 @@ namespace moe {
 
 // ---------------------------------------------------------------- fills
 struct FillArgs {
-  Dev v;
-  const uint4* pool;  // device mapping of the pinned pool
+  const int* hdr;        // plan header (HDR_NMISS misses)
+  const int* miss_key;   // [misses] pool key of each miss
+  const int* miss_slot;  // [misses] destination slot
+  const uint4* pool;     // device mapping of the pinned pool
   uint4* arena;
-  long long S16;      // blob bytes / 16
+  long long S16;         // blob bytes / 16
   int group;
   int ngroups;
 };
@@ -36,15 +38,15 @@ constexpr int FILL_THREADS = 256;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(FILL_THREADS) void fill_kernel(FillArgs a) {
-  const int m = a.v.hdr[HDR_NMISS];
+  const int m = a.hdr[HDR_NMISS];
   const int n0 = (int)((long long)a.group * m / a.ngroups);
   const int n1 = (int)((long long)(a.group + 1) * m / a.ngroups);
   const size_t tid = (size_t)blockIdx.x * FILL_THREADS + threadIdx.x;
   const size_t nthr = (size_t)gridDim.x * FILL_THREADS;
   const size_t S16 = (size_t)a.S16;
   for (int b = n0; b < n1; ++b) {
-    const uint4* src = a.pool + (size_t)a.v.miss_key[b] * S16;
-    uint4* dst = a.arena + (size_t)a.v.miss_slot[b] * S16;
+    const uint4* src = a.pool + (size_t)a.miss_key[b] * S16;
+    uint4* dst = a.arena + (size_t)a.miss_slot[b] * S16;
     for (size_t i = tid; i < S16; i += 4 * nthr) {
       uint4 r[4];
 #pragma unroll
@@ -62,9 +64,13 @@ __global__ __launch_bounds__(FILL_THREADS) void fill_kernel(FillArgs a) {
   }
 }
 
+// Copies the misses of a plan (`prefetch`: the prefetch plan, else the step plan).
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
-                       int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  FillArgs a{v, (const uint4*)pool_dev, (uint4*)arena, S / 16, group, ngroups};
+                       int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                       int prefetch, int E) {
+  const PlanOut o = prefetch ? prefetch_plan_out(v, E) : step_plan_out(v);
+  FillArgs a{o.hdr, o.miss_key, o.miss_slot, (const uint4*)pool_dev, (uint4*)arena, S / 16,
+             group, ngroups};
   return launch_timed(fill_kernel, dim3(grid), dim3(FILL_THREADS), 0, s, e0, e1, a);
 }
 

@@ -114,7 +114,40 @@ struct Dev {
   int* row_tok;        // [amax] token of each expert-sorted assignment row
   float* row_w;        // [amax] routing weight of each row
   int* moves;          // [max_capacity * 2] resize moves (src, dst)
+  // plan of a prefetch step (every expert of the next layer; steps of many tokens only),
+  // kept apart from the step plan that the FFN may still be reading
+  int* pf_hdr;         // [HDR_WORDS]
+  int* pf_list;        // [11 * E + 1]: U, u_slot, u_hit, hit_list, miss_list, miss_key,
+                       //   miss_slot, miss_victim, count, offset[E + 1]
+  int4* pf_ent;        // [E]
 };
+
+// Where a plan writes its outputs: the step plan or a prefetch plan.
+struct PlanOut {
+  int* U;
+  int* u_slot;
+  int* u_hit;
+  int* hit_list;
+  int* miss_list;
+  int* miss_key;
+  int* miss_slot;
+  int* miss_victim;
+  int* count;
+  int* offset;
+  int4* ent;
+  int* hdr;
+};
+
+__host__ __device__ inline PlanOut step_plan_out(const Dev& v) {
+  return PlanOut{v.U,         v.u_slot,      v.u_hit, v.hit_list, v.miss_list, v.miss_key,
+                 v.miss_slot, v.miss_victim, v.count, v.offset,   v.ent,       v.hdr};
+}
+
+__host__ __device__ inline PlanOut prefetch_plan_out(const Dev& v, int E) {
+  int* b = v.pf_list;
+  return PlanOut{b,         b + E,     b + 2 * E, b + 3 * E, b + 4 * E, b + 5 * E,
+                 b + 6 * E, b + 7 * E, b + 8 * E, b + 9 * E, v.pf_ent,  v.pf_hdr};
+}
 
 constexpr int kMaxFillGroups = 64;
 

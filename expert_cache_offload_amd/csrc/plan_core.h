@@ -143,36 +143,38 @@ __device__ inline void plan_begin(const Dims& d, const Dev& v, int layer, PlanLd
 
 // After s.cnt holds the step's assignments per expert (synced): U ascending (ballot /
 // popcount compaction), count/offset per position in U; returns nU.  Ends synced.
-__device__ inline int plan_dedup(const Dims& d, const Dev& v, PlanLds& s, PlanTmp& pt) {
+__device__ inline int plan_dedup(const Dims& d, const PlanOut& o, PlanLds& s, PlanTmp& pt) {
   const int nU = block_compact(
       d.E, [&](int e) { return s.cnt[e] > 0; },
       [&](int e, int pos) {
         s.U[pos] = e;
         s.uidx[e] = pos;
-        v.U[pos] = e;
+        o.U[pos] = e;
       },
       pt.tmp);
   if (threadIdx.x == 0) {
     int run = 0;
     for (int u = 0; u < nU; ++u) {
       s.off[u] = run;
-      v.offset[u] = run;
+      o.offset[u] = run;
       const int c = s.cnt[s.U[u]];
-      v.count[u] = c;
+      o.count[u] = c;
       run += c;
     }
     s.off[nU] = run;
-    v.offset[nU] = run;
+    o.offset[nU] = run;
   }
   __syncthreads();
   return nU;
 }
 
-// Classification, LRU victims, slot-table update, entry table, header and counters.
-// Returns false (after recording the error and an empty plan) when fewer slots can be
-// evicted than there are misses.
-__device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T, int nU,
-                                  PlanLds& s, const PlanState& ps, PlanTmp& pt) {
+// Classification, LRU victims, slot-table update, entry table, header and counters, written
+// to `o`.  The slots prot[0 .. n_prot) are never victims (a prefetch protects the slots of the
+// step before it).  Returns false (after recording the error and an empty plan) when fewer
+// slots can be evicted than there are misses.
+__device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o, int layer,
+                                  int T, int nU, PlanLds& s, const PlanState& ps, PlanTmp& pt,
+                                  const int* prot = nullptr, int n_prot = 0) {
   const int E = d.E, umax = d.umax;
   for (int u = threadIdx.x; u < nU; u += RT) {
     const int sl = s.srow[s.U[u]];
@@ -183,7 +185,7 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T,
   const int nHit = block_compact(
       nU, [&](int u) { return s.hit[u] != 0; },
       [&](int u, int pos) {
-        v.hit_list[pos] = u;
+        o.hit_list[pos] = u;
         s.hitl[pos] = u;
       },
       pt.tmp);
@@ -191,7 +193,7 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T,
       nU, [&](int u) { return s.hit[u] == 0; },
       [&](int u, int pos) {
         s.miss[pos] = u;
-        v.miss_list[pos] = u;
+        o.miss_list[pos] = u;
       },
       pt.tmp);
 
@@ -212,6 +214,10 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T,
     __syncthreads();
     for (int u = threadIdx.x; u < nU; u += RT)  // keys of this step are never victims
       if (s.hit[u]) s.comp[s.uslot[u]] = NONE;
+    for (int i = threadIdx.x; i < n_prot; i += RT) {  // nor are protected slots
+      const int sl = prot[i];
+      if (sl >= 0 && sl < n) s.comp[sl] = NONE;
+    }
     __syncthreads();
     int got = 0;
     for (int round = 0; round < need && got < need; ++round) {
@@ -255,9 +261,9 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T,
   if (pt.err) {
     if (threadIdx.x == 0) {
       atomicOr(&v.ctrl[CTRL_ERR], ERR_CAPACITY);
-      v.hdr[HDR_NU] = 0;
-      v.hdr[HDR_NHIT] = 0;
-      v.hdr[HDR_NMISS] = 0;
+      o.hdr[HDR_NU] = 0;
+      o.hdr[HDR_NHIT] = 0;
+      o.hdr[HDR_NMISS] = 0;
     }
     return false;
   }
@@ -279,32 +285,32 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, int layer, int T,
     v.key_of[slot] = key;
     v.slot_of[key] = slot;
     s.uslot[u] = slot;
-    v.miss_key[i] = key;
-    v.miss_slot[i] = slot;
-    v.miss_victim[i] = s.avkey[i];
+    o.miss_key[i] = key;
+    o.miss_slot[i] = slot;
+    o.miss_victim[i] = s.avkey[i];
   }
   __syncthreads();
   for (int u = threadIdx.x; u < nU; u += RT) {
     v.stamp[s.uslot[u]] = (int)ps.step;
-    v.u_slot[u] = s.uslot[u];
-    v.u_hit[u] = s.hit[u];
+    o.u_slot[u] = s.uslot[u];
+    o.u_hit[u] = s.hit[u];
   }
   // FFN entry table: hits first, then misses in ascending expert id (the fill order)
   for (int g = threadIdx.x; g < nU; g += RT) {
     const int miss = g < nHit ? -1 : g - nHit;
     const int u = miss < 0 ? s.hitl[g] : s.miss[miss];
-    v.ent[g] = make_int4(s.uslot[u], s.cnt[s.U[u]], s.off[u], miss);
+    o.ent[g] = make_int4(s.uslot[u], s.cnt[s.U[u]], s.off[u], miss);
   }
   if (threadIdx.x == 0) {
     const int nn = n + nMiss;
     v.ctrl[CTRL_N] = nn < C ? nn : C;
-    v.hdr[HDR_NU] = nU;
-    v.hdr[HDR_NHIT] = nHit;
-    v.hdr[HDR_NMISS] = nMiss;
-    v.hdr[HDR_LAYER] = layer;
-    v.hdr[HDR_T] = T;
-    v.hdr[HDR_STEP_LO] = (int)(ps.step & 0xffffffff);
-    v.hdr[HDR_STEP_HI] = (int)(ps.step >> 32);
+    o.hdr[HDR_NU] = nU;
+    o.hdr[HDR_NHIT] = nHit;
+    o.hdr[HDR_NMISS] = nMiss;
+    o.hdr[HDR_LAYER] = layer;
+    o.hdr[HDR_T] = T;
+    o.hdr[HDR_STEP_LO] = (int)(ps.step & 0xffffffff);
+    o.hdr[HDR_STEP_HI] = (int)(ps.step >> 32);
     const long long ns = ps.step + 1;
     v.ctrl[CTRL_STEP_LO] = (int)(ns & 0xffffffff);
     v.ctrl[CTRL_STEP_HI] = (int)(ns >> 32);

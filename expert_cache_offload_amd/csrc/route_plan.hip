@@ -172,7 +172,8 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  const int nU = plan_dedup(d, v, s, pt);
+  const PlanOut o = step_plan_out(v);
+  const int nU = plan_dedup(d, o, s, pt);
   // per-expert assignment lists, ascending token inside an expert
   for (int i = threadIdx.x; i < A; i += RT) {
     const int e = s_tk_idx[i];
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     v.row_tok[pos] = i / K;
     v.row_w[pos] = s_tk_w[i];
   }
-  plan_cache(d, v, layer, T, nU, s, ps, pt);
+  plan_cache(d, v, o, layer, T, nU, s, ps, pt);
   if (threadIdx.x == 0)
     __hip_atomic_store(&v.ctrl[CTRL_TICKET], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

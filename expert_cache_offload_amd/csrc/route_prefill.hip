@@ -229,7 +229,8 @@ __global__ __launch_bounds__(RT) void prefill_plan_kernel(PrefRouteArgs a) {
     s.cnt[e] = run;
   }
   __syncthreads();
-  const int nU = plan_dedup(d, v, s, pt);
+  const PlanOut o = step_plan_out(v);
+  const int nU = plan_dedup(d, o, s, pt);
   // first expert-sorted row of each (block, expert): tokens stay ascending inside an expert
   for (int e = threadIdx.x; e < E; e += RT) {
     if (s.uidx[e] < 0) continue;
@@ -245,7 +246,27 @@ __global__ __launch_bounds__(RT) void prefill_plan_kernel(PrefRouteArgs a) {
       }
     }
   }
-  plan_cache(d, v, a.layer, a.T, nU, s, ps, pt);
+  plan_cache(d, v, o, a.layer, a.T, nU, s, ps, pt);
+}
+
+// Prefetch plan of layer a.layer: a plan step whose distinct set is every expert of the layer
+// (one workgroup), written to the prefetch plan area; the slots of the step plan just before
+// it (whose FFN may still be reading them) are protected from eviction.
+__global__ __launch_bounds__(RT) void prefetch_plan_kernel(PrefRouteArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Dims& d = a.d;
+  const Dev& v = a.v;
+  PlanLds s;
+  plan_carve(d, smem, s);
+  __shared__ PlanTmp pt;
+  PlanState ps;
+  plan_begin(d, v, a.layer, s, ps);
+  __syncthreads();
+  for (int e = threadIdx.x; e < d.E; e += RT) s.cnt[e] = 1;
+  __syncthreads();
+  const PlanOut o = prefetch_plan_out(v, d.E);
+  const int nU = plan_dedup(d, o, s, pt);
+  plan_cache(d, v, o, a.layer, 0, nU, s, ps, pt, v.u_slot, v.hdr[HDR_NU]);
 }
 
 __global__ __launch_bounds__(RT) void prefill_scatter_kernel(PrefRouteArgs a) {
@@ -279,6 +300,14 @@ static hipError_t launch_router(const PrefRouteArgs& a, hipStream_t s, hipEvent_
 }
 
 bool prefill_route_supported(const Dims& d) { return d.E <= 256 && d.K <= kMaxTopK; }
+
+hipError_t launch_prefetch_plan(const Dims& d, const Dev& v, int layer, hipStream_t s) {
+  PrefRouteArgs a{d, v, nullptr, nullptr, nullptr, nullptr, layer, 0};
+  const size_t lds = plan_lds_bytes(d);
+  hipError_t e = set_lds(prefetch_plan_kernel, lds);
+  if (e != hipSuccess) return e;
+  return launch_timed(prefetch_plan_kernel, dim3(1), dim3(RT), lds, s, nullptr, nullptr, a);
+}
 
 hipError_t launch_route_prefill(const Dims& d, const Dev& v, const void* x, const void* wr,
                                 int* out_idx, float* out_w, int layer, int T, hipStream_t s,

@@ -17,8 +17,8 @@ import moe_inputs as mi
 
 from . import (make_shape, moe_cache_create, moe_cache_destroy, moe_cache_resize,
                moe_cache_snapshot, moe_expert_ffn, moe_fill_misses, moe_host_pool_alloc,
-               moe_host_pool_free, moe_layer_step, moe_plan_read, moe_route_classify, moe_stats,
-               moe_workspace_bytes)
+               moe_host_pool_free, moe_layer_step, moe_plan_read, moe_route_classify,
+               moe_set_prefetch, moe_stats, moe_workspace_bytes)
 
 
 def pinned_view(addr: int, nbytes: int) -> np.ndarray:
@@ -115,6 +115,12 @@ class Workbench:
         self.handle = moe_cache_create(self.shape, self.capacity, self.max_capacity, self.arena,
                                        self.ws, self.pool_addr, self.compute.cuda_stream)
         self.sync()
+        if getattr(self, "prefetch", False):
+            moe_set_prefetch(self.handle, True)
+
+    def set_prefetch(self, enable: bool) -> None:
+        self.prefetch = bool(enable)
+        moe_set_prefetch(self.handle, self.prefetch)
 
     def sync(self) -> None:
         torch.cuda.synchronize(self.dev)

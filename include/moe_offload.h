@@ -189,6 +189,18 @@ moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int32_t* stamp,
                               int32_t* slot_of, int32_t* n_occupied, int64_t* step,
                               int32_t* capacity);
 
+/* Prefetch mode for steps of more than 8 tokens (prefill chunks), whose routing union
+ * covers nearly every expert ("FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理", on the prefill
+ * union crossing PCIe): each moe_layer_step of layer l (l + 1 < layers) also plans a
+ * prefetch step of layer l + 1 - an LRU step whose distinct set is every expert of l + 1,
+ * with the slots of step l protected from eviction, taking its own step-counter value - and
+ * copies its misses on fill_stream while step l's FFN runs; step l + 1's FFN waits for
+ * them.  The caller's next layer step must then be layer l + 1.  Decode steps (T <= 8) never
+ * prefetch.  enable: 0 or 1.  MOE_E_INVALID for a handle with max_tokens <= 8; MOE_E_BUSY
+ * while a step or a prefetch is in flight (moe_cache_resize is MOE_E_BUSY too until the
+ * prefetched layer's step has run). */
+moe_status moe_set_prefetch(moe_cache cache, int32_t enable);
+
 /* Synchronous copy of the last plan (see moe_plan_host). */
 moe_status moe_plan_read(moe_cache cache, moe_plan_host* out);
 

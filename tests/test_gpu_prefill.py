@@ -46,6 +46,55 @@ def _run_chunk(wb, ffn_layers=None, state=True):
     return errs
 
 
+def _run_chunk_prefetch(wb):
+    """Layer steps with prefetch of the next layer: every step against the oracle's step, the
+    cache state after each call against the oracle after the step and the prefetch."""
+    wl = wb.wl
+    orc = _oracle(wb)
+    wb.set_prefetch(True)
+    errs = []
+    for l in range(wl.layers):
+        wb.step(0, l)
+        ref = orc.layer_step(0, l, wb.acts_np[l], True)
+        errs.append(compare_step(wb, ref, f"{wl.name} prefetch l={l}", check_state=False))
+        if l > 0:
+            assert not ref.rec.misses, "the prefetched layer should route to hits only"
+        if l + 1 < wl.layers:
+            orc.prefetch(l + 1, l, ref.U)
+        key_of, stamp, slot_of, n, step, cap = wb.snapshot()
+        assert n == orc.cache.n and step == orc.s, (l, n, orc.cache.n, step, orc.s)
+        assert list(key_of) == orc.cache.key_of, l
+        assert list(stamp) == orc.cache.stamp, l
+        for sl, k in enumerate(orc.cache.key_of):
+            if k >= 0:
+                assert slot_of[k] == sl
+    return [e for e in errs if e is not None]
+
+
+@pytest.mark.parametrize("groups", [0, 3])
+def test_prefill_prefetch_tiny(groups):
+    """Prefetch of the next layer at the tiny shape with a shared expert: 100 tokens, 4 layers,
+    40 slots (a layer's 16 experts plus the protected 16 of the step before fit)."""
+    base = dataclasses.replace(mi.WORKLOADS["tiny"], layers=4, fixed_capacity=40, has_shared=True)
+    wl = base.as_prefill(100)
+    _log(f"case {wl.name} prefetch groups={groups}")
+    with _bench(wl, groups=groups) as wb:
+        errs = _run_chunk_prefetch(wb)
+    _log(f"tiny prefetch: max rel-L2 {max(errs):.2e}")
+
+
+def test_prefill_prefetch_qwen_shape():
+    """Prefetch at the 35B expert shape: 300 tokens over 5 layers with 300 slots, so the
+    prefetches evict (the protected keys of the step before are never taken)."""
+    wl = dataclasses.replace(mi.WORKLOADS["qwen35b_prefill"].with_layers(5).with_tokens(300),
+                             fixed_capacity=300)
+    _log(f"case {wl.name} prefetch C={wl.capacity}")
+    with _bench(wl, groups=0) as wb:
+        errs = _run_chunk_prefetch(wb)
+        st = wb.stats()
+    _log(f"qwen prefetch: max rel-L2 {max(errs):.2e}, misses {st['misses']}")
+
+
 def test_prefill_tiny_shape_with_shared_expert():
     """16 experts top-2 at hidden 256: 100 tokens (one full and one ragged 64-token block,
     row tiles far from full), three layers over 24 slots so the later layers evict."""
