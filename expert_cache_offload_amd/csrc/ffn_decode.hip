@@ -78,11 +78,6 @@ struct Fmt<FMT_BF16> {
   static constexpr int DC = 8;   // down-projection columns per thread load (16 bytes)
   static constexpr int SB = 0;   // no scale blocks
   __device__ static size_t row_bytes(int n) { return (size_t)n * 2; }
-  __device__ static void unpack(uint4 w, float* f) {
-    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
-  }
-  __device__ static void load_d(const unsigned char* p, float* f) { unpack(*(const uint4*)p, f); }
 };
 
 template <>
@@ -91,10 +86,6 @@ struct Fmt<FMT_FP8> {
   static constexpr int DC = 16;  // 16 bytes
   static constexpr int SB = 128;
   __device__ static size_t row_bytes(int n) { return (size_t)n; }
-  __device__ static void unpack(uint4 w, float* f) {
-    fp8x4(w.x, f); fp8x4(w.y, f + 4); fp8x4(w.z, f + 8); fp8x4(w.w, f + 12);
-  }
-  __device__ static void load_d(const unsigned char* p, float* f) { unpack(*(const uint4*)p, f); }
 };
 
 template <>
@@ -103,30 +94,7 @@ struct Fmt<FMT_MXFP4> {
   static constexpr int DC = 16;  // 8 bytes: keeps the down accumulators in registers
   static constexpr int SB = 32;
   __device__ static size_t row_bytes(int n) { return (size_t)n / 2; }
-  __device__ static void unpack(uint4 w, float* f) {
-    fp4x8(w.x, f); fp4x8(w.y, f + 8); fp4x8(w.z, f + 16); fp4x8(w.w, f + 24);
-  }
-  __device__ static void load_d(const unsigned char* p, float* f) {
-    const uint2 w = *(const uint2*)p;
-    fp4x8(w.x, f);
-    fp4x8(w.y, f + 8);
-  }
 };
-
-// Scale of gate (g=0) / up (g=1) row i at contraction position xp.
-template <int FMT>
-__device__ __forceinline__ float gu_scale(const unsigned char* blob, int H, int I, int i, int g,
-                                          int xp) {
-  if constexpr (FMT == FMT_FP8) {
-    const float* s = (const float*)(blob + (size_t)3 * I * H);
-    return s[(size_t)(2 * i + g) * (H / 128) + xp / 128];
-  } else if constexpr (FMT == FMT_MXFP4) {
-    const unsigned char* s = blob + (size_t)3 * I * H / 2;
-    return e8m0_to_f32(s[(size_t)(2 * i + g) * (H / 32) + xp / 32]);
-  } else {
-    return 1.0f;
-  }
-}
 
 // Scales of the down-projection block `blk` for DC consecutive columns starting at c.
 template <int FMT>
@@ -213,15 +181,141 @@ __device__ __forceinline__ bool resolve(const FfnArgs& a, int j, Entry& en) {
 }
 
 // ---------------------------------------------------------------- gate / up role
-// No LDS and no barrier: every wave owns two rows, puts all of its weight loads in flight
-// first (the chain hdr -> entry -> slot is the only dependency), then reads the token
-// activations (a few KiB, shared by all waves through the L1) and reduces across the wave.
-constexpr int GPF = 8;  // 16-byte chunks per lane per row kept in flight
+// No barrier at one token: every wave owns two rows (i0 and i0 + 4 of the workgroup's
+// eight).  Lane l takes the gate chunks l, l + 64, ... of both rows and the up chunks at the
+// same contraction positions, so one set of activations serves four weight chunks.  The
+// lane's activations go out first (at one token they do not depend on the plan), then every
+// weight chunk and scale of the pass; loads complete in issue order, so nothing waits on a
+// later load.  Products use gfx950's two-wide bf16 dot (fp8 and e2m1 codes are widened to
+// bf16 first, exactly); per-chunk block scales multiply the chunk's sum.  At more tokens the
+// routed tokens' activations are staged in LDS once per workgroup.
+constexpr int GN = 4;  // gate chunks per lane per pass (4 * GN weight loads in flight)
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w),
+                                         __builtin_bit_cast(bf16x2v, x), acc, false);
+}
+__device__ __forceinline__ float dot2(bf16x2v w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2v, x), acc, false);
+}
+
+// sum over one 16-byte weight chunk (EPL weights, unscaled codes) times EPL activations
+// given as EPL/2 words of bf16 pairs; acc is added
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(const u32x4v& w, const uint32_t* xw, float acc);
+template <>
+__device__ __forceinline__ float chunk_dot<FMT_BF16>(const u32x4v& w, const uint32_t* xw,
+                                                     float acc) {
+  acc = dot2(w.x, xw[0], acc);
+  acc = dot2(w.y, xw[1], acc);
+  acc = dot2(w.z, xw[2], acc);
+  return dot2(w.w, xw[3], acc);
+}
+template <>
+__device__ __forceinline__ float chunk_dot<FMT_FP8>(const u32x4v& w, const uint32_t* xw,
+                                                    float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, false), xw[2 * q], acc);
+    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, true), xw[2 * q + 1], acc);
+  }
+  return acc;
+}
+template <>
+__device__ __forceinline__ float chunk_dot<FMT_MXFP4>(const u32x4v& w, const uint32_t* xw,
+                                                      float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 0), xw[4 * q], acc);
+    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 1), xw[4 * q + 1], acc);
+    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 2), xw[4 * q + 2], acc);
+    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 3), xw[4 * q + 3], acc);
+  }
+  return acc;
+}
+
+// scale of gate (g = 0) or up (g = 1) row i for the 16-byte chunk c of that half-row
+template <int FMT>
+__device__ __forceinline__ float gu_chunk_scale(const unsigned char* blob, int H, int I, int i,
+                                                int g, int c) {
+  if constexpr (FMT == FMT_FP8) {
+    const float* s = (const float*)(blob + (size_t)3 * I * H);
+    return s[(size_t)(2 * i + g) * (H / 128) + c / 8];  // 8 chunks of 16 codes per block
+  } else if constexpr (FMT == FMT_MXFP4) {
+    const unsigned char* s = blob + (size_t)3 * I * H / 2;
+    return e8m0_to_f32(s[(size_t)(2 * i + g) * (H / 32) + c]);  // one 32-code block per chunk
+  } else {
+    return 1.0f;
+  }
+}
+
+// Butterfly reduce-scatter over the wave of M = 2 * NTOK units (gate, up): afterwards lane l
+// holds the wave total of unit gu_unit<NTOK>(l) (every lane sharing that unit holds it).
+template <int NTOK>
+__device__ __forceinline__ void wave_reduce_units(float* gv, float* uv, int lane) {
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int o = 32 >> st, n = (2 * NTOK) >> st;
+    if (n > 1) {
+      const int half = n / 2;
+      const bool hi = (lane & o) != 0;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        // opaque copies: keeps the lane-dependent choice a register select (a select of two
+        // array loads would otherwise become a dynamically indexed private array)
+        float ga = gv[i], gb = gv[half + i], ua = uv[i], ub = uv[half + i];
+        asm volatile("" : "+v"(ga), "+v"(gb), "+v"(ua), "+v"(ub));
+        const float sg = hi ? ga : gb, kg = hi ? gb : ga;
+        const float su = hi ? ua : ub, ku = hi ? ub : ua;
+        gv[i] = kg + __shfl_xor(sg, o);
+        uv[i] = ku + __shfl_xor(su, o);
+      }
+    } else {
+      gv[0] += __shfl_xor(gv[0], o);
+      uv[0] += __shfl_xor(uv[0], o);
+    }
+  }
+}
+template <int NTOK>
+__device__ __forceinline__ int gu_unit(int lane) {
+  int m = 0;
+#pragma unroll
+  for (int st = 0; st < 6; ++st) {
+    const int o = 32 >> st, n = (2 * NTOK) >> st;
+    if (n > 1 && (lane & o)) m += n / 2;
+  }
+  return m;
+}
+
+template <int FMT>
+struct GuX {  // 16-byte activation vectors per weight chunk
+  static constexpr int XV = Fmt<FMT>::EPL / 8;
+};
+
+// At one token: the lane's activations of pass kb (gate chunks c = (kb + k) * 64 + lane).
+template <int FMT>
+__device__ __forceinline__ void load_x1(const FfnArgs& a, int kb, int lane,
+                                        u32x4v (&xr)[GN][GuX<FMT>::XV]) {
+  constexpr int EPL = Fmt<FMT>::EPL, XV = GuX<FMT>::XV;
+  const int ngq = a.d.H / EPL;
+#pragma unroll
+  for (int k = 0; k < GN; ++k) {
+    int c = (kb + k) * 64 + lane;
+    c = c < ngq ? c : ngq - 1;
+    const u32x4v* p = (const u32x4v*)(a.x + (size_t)c * EPL);
+#pragma unroll
+    for (int q = 0; q < XV; ++q) xr[k][q] = p[q];
+  }
+}
 
 template <int FMT, int NTOK>
-__device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb) {
+__device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
+                             u32x4v (&xr)[GN][GuX<FMT>::XV], uint16_t* s_x) {
   using F = Fmt<FMT>;
-  constexpr int EPL = F::EPL;
+  constexpr int EPL = F::EPL, XV = GuX<FMT>::XV;
   const Dims& d = a.d;
   const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -230,132 +324,159 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb) {
     atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
     if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_BLOB_BYTES], (unsigned long long)d.S);
   }
-  const int i0 = rb * RA + wave, i1 = i0 + 4;
-  const size_t rbytes = F::row_bytes(2 * H);
-  const uint4* row0 = (const uint4*)(en.blob + (size_t)i0 * rbytes);
-  const uint4* row1 = (const uint4*)(en.blob + (size_t)i1 * rbytes);
-  const int nq = 2 * H / EPL;          // 16-byte chunks per row
-  const int nper = (nq + 63) / 64;     // per lane
+  // routed tokens and their weights first: they are the only loads the activations wait on
   int tok[NTOK];
   float wt[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
-    tok[t] = 0;
-    wt[t] = 0.f;
+    const int tc = t < ntok ? t : 0;
+    tok[t] = en.shared ? tc : a.v.row_tok[en.row0 + tc];
+    wt[t] = en.shared ? 1.0f : a.v.row_w[en.row0 + tc];
   }
+  const int i0 = rb * RA + wave, i1 = i0 + 4;
+  const size_t rbytes = F::row_bytes(2 * H), hbytes = F::row_bytes(H);
+  const unsigned char* r0 = en.blob + (size_t)i0 * rbytes;
+  const unsigned char* r1 = en.blob + (size_t)i1 * rbytes;
+  const int ngq = H / EPL;  // 16-byte chunks per half-row (gate or up)
   float g0[NTOK], u0[NTOK], g1[NTOK], u1[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) g0[t] = u0[t] = g1[t] = u1[t] = 0.f;
-  for (int base = 0; base < nper; base += GPF) {
-    uint4 w0[GPF], w1[GPF];
+  for (int kb = 0; kb * 64 < ngq; kb += GN) {
+    u32x4v wg0[GN], wu0[GN], wg1[GN], wu1[GN];
+    float sg0[GN], su0[GN], sg1[GN], su1[GN];  // block scales (fp8, MXFP4)
 #pragma unroll
-    for (int k = 0; k < GPF; ++k) {
-      if ((base + k) * 64 + lane < nq) {
-        w0[k] = row0[(base + k) * 64 + lane];
-        w1[k] = row1[(base + k) * 64 + lane];
+    for (int k = 0; k < GN; ++k) {
+      int c = (kb + k) * 64 + lane;
+      c = c < ngq ? c : ngq - 1;  // in-row address; masked below
+      wg0[k] = *(const u32x4v*)(r0 + (size_t)c * 16);
+      wu0[k] = *(const u32x4v*)(r0 + hbytes + (size_t)c * 16);
+      wg1[k] = *(const u32x4v*)(r1 + (size_t)c * 16);
+      wu1[k] = *(const u32x4v*)(r1 + hbytes + (size_t)c * 16);
+    }
+    if constexpr (F::SB > 0) {
+#pragma unroll
+      for (int k = 0; k < GN; ++k) {
+        int c = (kb + k) * 64 + lane;
+        c = c < ngq ? c : ngq - 1;
+        sg0[k] = gu_chunk_scale<FMT>(en.blob, H, I, i0, 0, c);
+        su0[k] = gu_chunk_scale<FMT>(en.blob, H, I, i0, 1, c);
+        sg1[k] = gu_chunk_scale<FMT>(en.blob, H, I, i1, 0, c);
+        su1[k] = gu_chunk_scale<FMT>(en.blob, H, I, i1, 1, c);
       }
     }
-    if (base == 0) {
+    if constexpr (NTOK == 1) {
+      if (kb > 0) load_x1<FMT>(a, kb, lane, xr);
+    } else {
+      // stage the pass's activations of every routed token: [t][GN * 64 chunks of EPL]
+      __syncthreads();  // previous pass done with s_x
+      constexpr int PC = GN * 64;  // chunks per token per pass
+      for (int idx = threadIdx.x; idx < NTOK * PC * XV; idx += FT) {
+        const int t = idx / (PC * XV), r = idx % (PC * XV);
+        const int c = kb * 64 + r / XV;
+        const int cc = c < ngq ? c : ngq - 1;
+        const int tt = t < ntok ? t : 0;
+        int tk = tok[0];
 #pragma unroll
-      for (int t = 0; t < NTOK; ++t) {
-        if (t < ntok) {
-          tok[t] = en.shared ? t : a.v.row_tok[en.row0 + t];
-          wt[t] = en.shared ? 1.0f : a.v.row_w[en.row0 + t];
-        }
+        for (int q = 1; q < NTOK; ++q) tk = tt == q ? tok[q] : tk;
+        const u32x4v v = *(const u32x4v*)(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8);
+        *(u32x4v*)(s_x + ((size_t)t * PC * XV + r) * 8) = v;
       }
+      __syncthreads();
     }
 #pragma unroll
-    for (int k = 0; k < GPF; ++k) {
-      if ((base + k) * 64 + lane < nq) {
-        const int p = ((base + k) * 64 + lane) * EPL;
-        const bool isg = p < H;
-        const int xp = isg ? p : p - H;
-        float f0[EPL], f1[EPL];
-        F::unpack(w0[k], f0);
-        F::unpack(w1[k], f1);
-        const float s0 = gu_scale<FMT>(en.blob, H, I, i0, isg ? 0 : 1, xp);
-        const float s1 = gu_scale<FMT>(en.blob, H, I, i1, isg ? 0 : 1, xp);
+    for (int k = 0; k < GN; ++k) {
+      const int c = (kb + k) * 64 + lane;
+      if (c < ngq) {
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
           if (t < ntok) {
-            const uint4* xv = (const uint4*)(a.x + (size_t)tok[t] * H + xp);
-            float d0 = 0.f, d1 = 0.f;
+            uint32_t xw[EPL / 2];
+            if constexpr (NTOK == 1) {
 #pragma unroll
-            for (int c8 = 0; c8 < EPL / 8; ++c8) {
-              const uint4 xx = xv[c8];
-              const float xf[8] = {bf16_lo(xx.x), bf16_hi(xx.x), bf16_lo(xx.y), bf16_hi(xx.y),
-                                   bf16_lo(xx.z), bf16_hi(xx.z), bf16_lo(xx.w), bf16_hi(xx.w)};
+              for (int q = 0; q < XV; ++q) {
+                xw[4 * q] = xr[k][q].x; xw[4 * q + 1] = xr[k][q].y;
+                xw[4 * q + 2] = xr[k][q].z; xw[4 * q + 3] = xr[k][q].w;
+              }
+            } else {
+              const u32x4v* sp =
+                  (const u32x4v*)(s_x + ((size_t)t * GN * 64 * XV + (size_t)(k * 64 + lane) * XV) * 8);
 #pragma unroll
-              for (int c = 0; c < 8; ++c) {
-                d0 += f0[c8 * 8 + c] * xf[c];
-                d1 += f1[c8 * 8 + c] * xf[c];
+              for (int q = 0; q < XV; ++q) {
+                const u32x4v v = sp[q];
+                xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
               }
             }
-            d0 *= s0;
-            d1 *= s1;
-            if (isg) {
-              g0[t] += d0;
-              g1[t] += d1;
+            if constexpr (F::SB > 0) {
+              g0[t] += sg0[k] * chunk_dot<FMT>(wg0[k], xw, 0.f);
+              u0[t] += su0[k] * chunk_dot<FMT>(wu0[k], xw, 0.f);
+              g1[t] += sg1[k] * chunk_dot<FMT>(wg1[k], xw, 0.f);
+              u1[t] += su1[k] * chunk_dot<FMT>(wu1[k], xw, 0.f);
             } else {
-              u0[t] += d0;
-              u1[t] += d1;
+              g0[t] = chunk_dot<FMT>(wg0[k], xw, g0[t]);
+              u0[t] = chunk_dot<FMT>(wu0[k], xw, u0[t]);
+              g1[t] = chunk_dot<FMT>(wg1[k], xw, g1[t]);
+              u1[t] = chunk_dot<FMT>(wu1[k], xw, u1[t]);
             }
           }
         }
       }
     }
   }
-  float* act = en.shared ? a.v.act_shared : a.v.act;
+  // units m = r * NTOK + t: (gate, up) of row r (i0 or i1) for token t
+  float gv[2 * NTOK], uv[2 * NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
-    if (t < ntok) {
-      float a0 = g0[t], b0 = u0[t], a1 = g1[t], b1 = u1[t];
-      for (int off = 32; off > 0; off >>= 1) {
-        a0 += __shfl_xor(a0, off);
-        b0 += __shfl_xor(b0, off);
-        a1 += __shfl_xor(a1, off);
-        b1 += __shfl_xor(b1, off);
-      }
-      if (lane == 0) {
-        float* out = act + (size_t)(en.row0 + t) * I;
-        out[i0] = silu(a0) * b0 * wt[t];
-        out[i1] = silu(a1) * b1 * wt[t];
-      }
-    }
+    gv[t] = g0[t]; uv[t] = u0[t];
+    gv[NTOK + t] = g1[t]; uv[NTOK + t] = u1[t];
+  }
+  wave_reduce_units<NTOK>(gv, uv, lane);
+  const int m = gu_unit<NTOK>(lane);
+  const int t = m % NTOK;
+  if ((lane & (64 / (2 * NTOK) - 1)) == 0 && t < ntok) {
+    float w = wt[0];
+#pragma unroll
+    for (int q = 1; q < NTOK; ++q) w = t == q ? wt[q] : w;
+    float* act = en.shared ? a.v.act_shared : a.v.act;
+    act[(size_t)(en.row0 + t) * I + (m < NTOK ? i0 : i1)] = silu(gv[0]) * uv[0] * w;
   }
 }
 
 // ---------------------------------------------------------------- down role
 // A workgroup owns a column block of DTC*DC columns of the stored transpose WdT and I/RS of
 // its rows; thread (row lane rl, column lane cl) owns DC columns of a contiguous run of at
-// most DMAXR rows.  All of a thread's weight loads go out first; the activations (fp32,
-// L1-shared) follow, then row lanes reduce by shuffles and through LDS across waves.  The
-// workgroup writes one partial sum per row split; the combine adds the splits.
+// most DMAXR rows.  The thread's activations go out first (fp32 rows written by the gate/up
+// kernel; at more than one token they are staged in LDS for the workgroup), then all of its
+// weight loads, so no load waits behind another; row lanes reduce by shuffles and through
+// LDS across waves.  The workgroup writes one partial sum per row split; the combine adds
+// the splits.
 constexpr int DTC = 16;            // column lanes
 constexpr int DTR = FT / DTC;      // row lanes
 constexpr int DMAXR = 16;          // rows per thread, at most
 
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 template <int FMT>
 struct DVec {
-  using T = uint4;
+  using T = u32x4v;
 };
 template <>
 struct DVec<FMT_MXFP4> {
-  using T = uint2;
+  using T = u32x2v;
 };
 
 template <int FMT>
 __device__ __forceinline__ void unpack_d(const typename DVec<FMT>::T& w, float* f);
 template <>
-__device__ __forceinline__ void unpack_d<FMT_BF16>(const uint4& w, float* f) {
-  Fmt<FMT_BF16>::unpack(w, f);
+__device__ __forceinline__ void unpack_d<FMT_BF16>(const u32x4v& w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 template <>
-__device__ __forceinline__ void unpack_d<FMT_FP8>(const uint4& w, float* f) {
-  Fmt<FMT_FP8>::unpack(w, f);
+__device__ __forceinline__ void unpack_d<FMT_FP8>(const u32x4v& w, float* f) {
+  fp8x4(w.x, f); fp8x4(w.y, f + 4); fp8x4(w.z, f + 8); fp8x4(w.w, f + 12);
 }
 template <>
-__device__ __forceinline__ void unpack_d<FMT_MXFP4>(const uint2& w, float* f) {
+__device__ __forceinline__ void unpack_d<FMT_MXFP4>(const u32x2v& w, float* f) {
   fp4x8(w.x, f);
   fp4x8(w.y, f + 8);
 }
@@ -375,13 +496,32 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
   const int cl = threadIdx.x % DTC, rl = threadIdx.x / DTC;
   const int c0 = cb * HC + cl * DC;
   const int ra = rs * IR + rl * nrw;
+  const float* act = (en.shared ? a.v.act_shared : a.v.act) + (size_t)en.row0 * I;
+  float* s_red = (float*)smem;                  // [4][NTOK][HC]
+  float* s_act = s_red + (size_t)4 * NTOK * HC;  // [NTOK][IR] (NTOK > 1)
+  // activations first
+  float av[DMAXR];
+  constexpr int SA = (NTOK * 256 + FT - 1) / FT;  // staged values per thread (IR <= 256)
+  float sv[NTOK > 1 ? SA : 1];
+  if constexpr (NTOK == 1) {
+#pragma unroll
+    for (int r = 0; r < DMAXR; ++r) av[r] = act[ra + (r < nrw ? r : nrw - 1)];
+  } else {
+#pragma unroll
+    for (int q = 0; q < SA; ++q) {
+      int idx = threadIdx.x + q * FT;
+      const int t = idx / IR, r = idx % IR;
+      const int tc = t < ntok ? t : 0;
+      sv[q] = act[(size_t)tc * I + rs * IR + r];
+    }
+  }
+  // then every weight row of the thread (clamped to its run; extra rows are not used)
   const unsigned char* wdt = en.blob + F::row_bytes(2 * H) * (size_t)I;  // WdT after Wgu
   const size_t drow = F::row_bytes(H);
   const unsigned char* wp = wdt + (size_t)ra * drow + F::row_bytes(c0);
   W w[DMAXR];
 #pragma unroll
-  for (int r = 0; r < DMAXR; ++r)
-    if (r < nrw) w[r] = *(const W*)(wp + (size_t)r * drow);
+  for (int r = 0; r < DMAXR; ++r) w[r] = *(const W*)(wp + (size_t)(r < nrw ? r : nrw - 1) * drow);
   float sc0[DC], sc1[DC];
   int bsplit = DMAXR;  // first r that uses sc1
   if constexpr (F::SB > 0) {
@@ -390,7 +530,14 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
     d_scales<FMT>(en.blob, H, I, blk1, c0, sc1);
     bsplit = (blk0 + 1) * F::SB - ra;
   }
-  const float* act = (en.shared ? a.v.act_shared : a.v.act) + (size_t)en.row0 * I + ra;
+  if constexpr (NTOK > 1) {
+#pragma unroll
+    for (int q = 0; q < SA; ++q) {
+      const int idx = threadIdx.x + q * FT;
+      if (idx < NTOK * IR) s_act[idx] = sv[q];
+    }
+    __syncthreads();
+  }
   float acc[NTOK][DC];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t)
@@ -408,15 +555,13 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
 #pragma unroll
       for (int t = 0; t < NTOK; ++t) {
         if (t < ntok) {
-          const float at = act[(size_t)t * I + r];
+          const float at = NTOK == 1 ? av[r] : s_act[t * IR + rl * nrw + r];
 #pragma unroll
           for (int c = 0; c < DC; ++c) acc[t][c] += at * f[c];
         }
       }
     }
   }
-  // reduce over the DTR row lanes: those inside a wave by shuffles, the 4 waves through LDS
-  float* s_red = (float*)smem;  // [4][NTOK][HC]
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
     if (t < ntok) {
@@ -447,9 +592,11 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
   }
 }
 
+
 // ---------------------------------------------------------------- combine role
 // y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + sum_rs yexp_shared[t][rs] ), in that fixed
-// order.
+// order.  Every partial of a chunk is loaded before any is added (one memory latency per
+// chunk of CH partials).
 __device__ void combine_role(const FfnArgs& a, int cblk) {
   const Dims& d = a.d;
   const Dev& v = a.v;
@@ -460,23 +607,23 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
   if ((int)threadIdx.x < d.K) s_pos[threadIdx.x] = v.inv_pos[t * d.K + threadIdx.x];
   __syncthreads();
   if (c >= d.H) return;
-  // all partials of a chunk are loaded before any is added: one memory latency per chunk
-  constexpr int CH = 16;
+  constexpr int CH = 32;
   const int RS = d.RS, nrouted = d.K * RS, nall = nrouted + (d.has_shared ? RS : 0);
   float s = 0.f;
   for (int base = 0; base < nall; base += CH) {
     float pv[CH];
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      const int i = base + q;
-      pv[q] = 0.f;
-      if (i < nrouted)
-        pv[q] = v.yexp[((size_t)s_pos[i / RS] * RS + i % RS) * d.H + c];
-      else if (i < nall)
-        pv[q] = v.yexp_shared[((size_t)t * RS + (i - nrouted)) * d.H + c];
+      int i = base + q;
+      i = i < nall ? i : nall - 1;
+      const float* p = i < nrouted
+                           ? v.yexp + ((size_t)s_pos[i / RS] * RS + i % RS) * d.H
+                           : v.yexp_shared + ((size_t)t * RS + (i - nrouted)) * d.H;
+      pv[q] = p[c];
     }
 #pragma unroll
-    for (int q = 0; q < CH; ++q) s += pv[q];
+    for (int q = 0; q < CH; ++q)
+      if (base + q < nall) s += pv[q];
   }
   a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
 }
@@ -488,10 +635,19 @@ static constexpr int down_hc() {
 
 template <int FMT, int NTOK>
 __global__ __launch_bounds__(FT) void ffn_gate_up_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
   const int nra = a.d.I / RA;
+  u32x4v xr[GN][GuX<FMT>::XV];
+  // at one token the activations do not depend on the plan: they go out before the entry
+  if constexpr (NTOK == 1) load_x1<FMT>(a, 0, threadIdx.x & 63, xr);
   Entry en;
   if (!resolve(a, blockIdx.x / nra, en)) return;
-  gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra);
+  gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra, xr, (uint16_t*)smem);
+}
+
+template <int FMT, int NTOK>
+static size_t gate_up_lds_bytes() {
+  return NTOK > 1 ? (size_t)NTOK * GN * 64 * Fmt<FMT>::EPL * 2 : 0;
 }
 
 template <int FMT, int NTOK>
@@ -532,10 +688,12 @@ static hipError_t launch_ffn(const FfnArgs& a, int stage, hipStream_t s, hipEven
   const Dims& d = a.d;
   constexpr int HC = down_hc<FMT>();
   if (stage == 0)
-    return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA), 0, a, s, e0, e1);
-  hipError_t e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS,
-                                 sizeof(float) * (size_t)4 * NTOK * HC, a, s, e0,
-                                 a.NC > 0 ? nullptr : e1);
+    return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA),
+                           gate_up_lds_bytes<FMT, NTOK>(), a, s, e0, e1);
+  const size_t dlds =
+      sizeof(float) * ((size_t)4 * NTOK * HC + (NTOK > 1 ? (size_t)NTOK * (d.I / d.RS) : 0));
+  hipError_t e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS, dlds, a,
+                                 s, e0, a.NC > 0 ? nullptr : e1);
   if (e != hipSuccess || a.NC <= 0) return e;
   return launch_timed(combine_kernel, dim3(a.NC), dim3(FT), 0, s, nullptr, e1, a);
 }
