@@ -34,6 +34,12 @@ R8  prefetch (steps of many tokens only): before layer l' is routed, a prefetch 
     step counter.  (FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理, on the prefill union:
     a long prefill routes to nearly every expert of every layer, so layer l' can be
     fetched while layer l computes.)
+R9  hybrid decode (CPU in-place compute of some misses): of the step's m misses, in
+    ascending expert id, the first m - q are filled as R3-R6 and the last q are computed
+    by the CPU straight from the host pool: they take no slot, evict nothing and are not
+    stamped (they are not cached), so need = max(0, m - q - (C - n)).  q comes from the
+    miss split (oracle/split.py).  (FreeToken paper summary: a decode miss is either moved
+    over PCIe or computed in place by the CPU; q is derived in the fused routing kernel.)
 R7  resize to C': if n <= C' nothing moves.  Otherwise the C' keys nearest the
     MRU end survive; holes in [0, C') are filled, in ascending slot order, by the
     survivors that sit in slots >= C', taken in ascending old-slot order; stamps
@@ -56,7 +62,8 @@ class StepRecord:
     U: list                  # distinct experts, ascending
     hit: list                # bool per entry of U
     slot: list               # cache slot per entry of U after the step
-    misses: list             # (key, slot, victim_key or -1) in ascending expert id
+    misses: list             # (key, slot, victim_key or -1) in ascending expert id, filled
+    cpu: list = field(default_factory=list)  # keys computed in place by the CPU (R9)
     key_of: list = field(default_factory=list)
     stamp: list = field(default_factory=list)
     n: int = 0
@@ -76,13 +83,18 @@ class LRUCache:
     def slot_of(self, key: int) -> int:
         return self.order.get(key, -1)
 
-    def step(self, layer: int, U, E: int, s: int, protected=()) -> StepRecord:
-        """R1-R6; `protected` keys are never victims either (R8)."""
+    def step(self, layer: int, U, E: int, s: int, protected=(), n_cpu: int = 0) -> StepRecord:
+        """R1-R6; `protected` keys are never victims either (R8); the last `n_cpu` misses
+        are computed by the CPU and not cached (R9)."""
         keys = [layer * E + int(e) for e in U]                          # R1 (U ascending)
         if len(keys) > self.C:
             raise CapacityError(f"{len(keys)} distinct experts exceed capacity {self.C}")
         hit = [key in self.order for key in keys]                       # R2
-        misses = [key for key, h in zip(keys, hit) if not h]             # R3
+        all_misses = [key for key, h in zip(keys, hit) if not h]         # R3
+        if not 0 <= n_cpu <= len(all_misses):
+            raise ValueError("n_cpu out of range")
+        misses = all_misses[:len(all_misses) - n_cpu]                    # R9
+        cpu = all_misses[len(all_misses) - n_cpu:]
         n_free = self.C - self.n
         need = max(0, len(misses) - n_free)                              # R4
         in_step = set(keys) | set(protected)
@@ -105,15 +117,18 @@ class LRUCache:
         for v in victims:                                                # R6
             del self.order[v]
         slot_of_new = {key: slot for key, slot, _ in assigned}
+        cpu_set = set(cpu)
         for key in keys:
+            if key in cpu_set:
+                continue
             slot = self.order.pop(key) if key in self.order else slot_of_new[key]
             self.order[key] = slot
             self.key_of[slot] = key
             self.stamp[slot] = s
         self.n = min(self.C, self.n + len(misses))
         return StepRecord(step=s, layer=layer, U=[int(e) for e in U], hit=hit,
-                          slot=[self.order[key] for key in keys], misses=assigned,
-                          key_of=list(self.key_of), stamp=list(self.stamp), n=self.n)
+                          slot=[self.order.get(key, -1) for key in keys], misses=assigned,
+                          cpu=cpu, key_of=list(self.key_of), stamp=list(self.stamp), n=self.n)
 
     def resize(self, new_capacity: int):
         """R7.  Returns the list of (old_slot, new_slot) moves, in ascending new slot."""

@@ -10,6 +10,9 @@ Step counter: s increments once per layer step; decode visits token step t
 outer and layer l inner (s = t * L + l); a prefill chunk visits layers in order.
 With prefetch (R8), a prefetch step of layer l + 1 follows the step of layer l and takes
 the next counter value.
+With a miss split (R9, decode steps of at most 8 tokens only), the last q of a step's misses
+are computed by the CPU and not cached, q = miss_split(m, b_cpu, b_pcie); the layer output is
+the same sum over the selected experts whichever device computes each.
 At decode all streams of a step (T tokens) share one dedup and one cache step.
 The resize happens at the safe point before token step ``resize_at``.
 """
@@ -24,6 +27,7 @@ from .ffn import moe_output
 from .formats import bf16_to_f64, decode_blob
 from .lru import LRUCache, StepRecord
 from .router import router_logits, topk_softmax
+from .split import miss_split
 
 
 @dataclass
@@ -47,13 +51,17 @@ class Oracle:
     pool      - uint8 array of L*E blobs (layer-major), or a callable key -> blob bytes
     router    - uint16 (bf16) array [L, E, H]
     shared    - optional callable layer -> shared-expert blob bytes
+    split     - optional (b_cpu, b_pcie) integer rates: hybrid decode (R9)
     """
 
-    def __init__(self, wl, pool, router, shared=None):
+    DECODE_MAX_TOKENS = 8
+
+    def __init__(self, wl, pool, router, shared=None, split=None):
         self.wl = wl
         self.pool = pool
         self.router = router
         self.shared = shared
+        self.split = split
         self.cache = LRUCache(wl.capacity, wl.n_keys)
         self.s = 0
 
@@ -73,7 +81,11 @@ class Oracle:
         z = router_logits(x, bf16_to_f64(self.router[layer]))
         idx, w = topk_softmax(z, wl.top_k)
         U, count, offset, perm = dedup(idx, wl.experts)
-        rec = self.cache.step(layer, U, wl.experts, self.s)
+        n_cpu = 0
+        if self.split is not None and x.shape[0] <= self.DECODE_MAX_TOKENS:
+            m = sum(1 for e in U if self.cache.slot_of(layer * wl.experts + int(e)) < 0)
+            n_cpu = miss_split(m, *self.split)
+        rec = self.cache.step(layer, U, wl.experts, self.s, n_cpu=n_cpu)
         y = None
         if with_ffn:
             decoded = {}
