@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_OFFLOAD_LIB") or os.path.join(_HERE, "libmoe_offload.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_CAPACITY, MOE_E_BUSY, MOE_E_HIP, MOE_E_NOMEM = 0, -1, -2, -3, -4, -5
+MOE_E_HYBRID = -6
 MOE_FMT_BF16, MOE_FMT_FP8_E4M3_K128, MOE_FMT_MXFP4_K32 = 0, 1, 2
 
 # PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7).  Loading torch
@@ -43,16 +44,18 @@ class MoeShape(ctypes.Structure):
 class MoePlanHost(ctypes.Structure):
     _fields_ = [("n_unique", ctypes.c_int32), ("n_hit", ctypes.c_int32),
                 ("n_miss", ctypes.c_int32), ("layer", ctypes.c_int32),
-                ("step", ctypes.c_int64),
+                ("step", ctypes.c_int64), ("n_cpu", ctypes.c_int32), ("pad_", ctypes.c_int32),
                 ("unique", ctypes.c_void_p), ("slot", ctypes.c_void_p),
                 ("hit", ctypes.c_void_p), ("miss_key", ctypes.c_void_p),
                 ("miss_slot", ctypes.c_void_p), ("miss_victim", ctypes.c_void_p),
-                ("count", ctypes.c_void_p), ("perm", ctypes.c_void_p)]
+                ("count", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("cpu_key", ctypes.c_void_p)]
 
 
 class MoeCounters(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("hits", ctypes.c_int64),
-                ("misses", ctypes.c_int64), ("bytes_filled", ctypes.c_int64)]
+                ("misses", ctypes.c_int64), ("bytes_filled", ctypes.c_int64),
+                ("cpu_misses", ctypes.c_int64)]
 
 
 class MoeProfile(ctypes.Structure):
@@ -85,6 +88,10 @@ _SIGS = {
     "moe_stats": (_i32, [_vp, ctypes.POINTER(MoeCounters)]),
     "moe_profile_enable": (_i32, [_vp, _i32, _i32]),
     "moe_set_prefetch": (_i32, [_vp, _i32]),
+    "moe_set_hybrid": (_i32, [_vp, _i32, _i32, _i32]),
+    "moe_cpu_expert_ffn": (_i32, [ctypes.POINTER(MoeShape), _vp, _vp, _i32, _vp, _vp, _i32]),
+    "moe_cpu_expert_rate": (_i32, [ctypes.POINTER(MoeShape), _vp, _i32, _i32, _i32,
+                                   ctypes.POINTER(ctypes.c_double)]),
     "moe_profile_read": (_i32, [_vp, ctypes.POINTER(MoeProfile)]),
     "moe_status_string": (ctypes.c_char_p, [_i32]),
     "moe_last_hip_error": (_i32, [_vp]),
@@ -203,9 +210,10 @@ def moe_plan_read(handle: int, max_unique: int, max_assign: int) -> dict:
             ("unique", "slot", "miss_key", "miss_slot", "miss_victim", "count")}
     bufs["hit"] = np.zeros(max_unique, np.uint8)
     bufs["perm"] = np.zeros(max(1, max_assign), np.int32)
-    ph = MoePlanHost(0, 0, 0, 0, 0, *[bufs[k].ctypes.data for k in
-                                      ("unique", "slot", "hit", "miss_key", "miss_slot",
-                                       "miss_victim", "count", "perm")])
+    bufs["cpu_key"] = np.zeros(max_unique, np.int32)
+    ph = MoePlanHost(0, 0, 0, 0, 0, 0, 0, *[bufs[k].ctypes.data for k in
+                                            ("unique", "slot", "hit", "miss_key", "miss_slot",
+                                             "miss_victim", "count", "perm", "cpu_key")])
     _check(_lib.moe_plan_read(handle, ctypes.byref(ph)), "moe_plan_read", handle)
     nu, nm = ph.n_unique, ph.n_miss
     return {"n_unique": nu, "n_hit": ph.n_hit, "n_miss": nm, "layer": ph.layer, "step": ph.step,
@@ -213,18 +221,49 @@ def moe_plan_read(handle: int, max_unique: int, max_assign: int) -> dict:
             "hit": bufs["hit"][:nu].astype(bool), "miss_key": bufs["miss_key"][:nm].copy(),
             "miss_slot": bufs["miss_slot"][:nm].copy(),
             "miss_victim": bufs["miss_victim"][:nm].copy(), "count": bufs["count"][:nu].copy(),
-            "perm": bufs["perm"].copy()}
+            "perm": bufs["perm"].copy(), "n_cpu": ph.n_cpu,
+            "cpu_key": bufs["cpu_key"][:ph.n_cpu].copy()}
 
 
 def moe_stats(handle: int) -> dict:
     c = MoeCounters()
     _check(_lib.moe_stats(handle, ctypes.byref(c)), "moe_stats", handle)
-    return {"steps": c.steps, "hits": c.hits, "misses": c.misses, "bytes_filled": c.bytes_filled}
+    return {"steps": c.steps, "hits": c.hits, "misses": c.misses, "bytes_filled": c.bytes_filled,
+            "cpu_misses": c.cpu_misses}
 
 
 def moe_set_prefetch(handle: int, enable: bool) -> None:
     """Prefetch the next layer's experts during steps of many tokens (see the header)."""
     _check(_lib.moe_set_prefetch(handle, int(bool(enable))), "moe_set_prefetch", handle)
+
+
+def moe_set_hybrid(handle: int, b_cpu_mbps: int, b_pcie_mbps: int, threads: int) -> None:
+    """Split decode misses between fills and in-place CPU compute (b_cpu_mbps 0: off)."""
+    _check(_lib.moe_set_hybrid(handle, int(b_cpu_mbps), int(b_pcie_mbps), int(threads)),
+           "moe_set_hybrid", handle)
+
+
+def moe_cpu_expert_ffn(shape: MoeShape, blob: int, x: int, T: int, w: int, y: int,
+                       threads: int) -> None:
+    """y[t] += w[t] * FFN(x[t]) on the host (host addresses)."""
+    _check(_lib.moe_cpu_expert_ffn(ctypes.byref(shape), blob, x, int(T), w, y, int(threads)),
+           "moe_cpu_expert_ffn")
+
+
+def moe_cpu_expert_rate(shape: MoeShape, pool: int, n_blobs: int, threads: int,
+                        reps: int = 1) -> float:
+    """Expert-weight GB/s of the CPU path over the first n_blobs blobs of a host pool."""
+    g = ctypes.c_double(0.0)
+    _check(_lib.moe_cpu_expert_rate(ctypes.byref(shape), pool, int(n_blobs), int(threads),
+                                    int(reps), ctypes.byref(g)), "moe_cpu_expert_rate")
+    return float(g.value)
+
+
+def choose_hybrid(cpu_gbps: float, offload_gbps: float, threshold: float = 2.0) -> bool:
+    """Mode choice per dtype: split misses with the CPU only when its expert rate is at
+    least `threshold` times the offload rate ("FreeToken: az VRAM ile büyük MoE modelleri",
+    "Tuzaklar": a 2.0x threshold)."""
+    return cpu_gbps > 0 and offload_gbps > 0 and cpu_gbps >= threshold * offload_gbps
 
 
 def moe_profile_enable(handle: int, mask: int = PROF_ALL, every: int = 1) -> None:
@@ -255,4 +294,4 @@ def moe_last_hip_error(handle: int) -> int:
 
 
 __all__ = [n for n in _SIGS] + ["MoeShape", "MoePlanHost", "MoeCounters", "MoeProfile", "MoeError",
-                                "make_shape", "LIB_PATH"]
+                                "make_shape", "choose_hybrid", "LIB_PATH"]

@@ -1,19 +1,24 @@
 // Host side of the C ABI declared in include/moe_offload.h: argument checks, workspace
 // layout, step orchestration across the compute and fill streams, resize and snapshots.
 #include <hip/hip_runtime.h>
+#include <immintrin.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "../../include/moe_offload.h"
+#include "cpu_expert.h"
 #include "moe_dev.h"
 
 namespace moe {
 hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const void* wr,
-                             int* out_idx, float* out_w, int layer, int T, hipStream_t s,
-                             hipEvent_t e0, hipEvent_t e1);
+                             int* out_idx, float* out_w, int layer, int T, int split_bc,
+                             int split_bp, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 size_t route_plan_lds_bytes(const Dims& d);
 hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const void* arena,
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
@@ -56,7 +61,7 @@ struct Layout {
   size_t key_of, stamp, slot_of, ctrl, stats, hdr, U, u_slot, u_hit, hit_list, miss_list,
       miss_key, miss_slot, miss_victim, count, offset, perm, inv_pos, tk_idx, tk_w, logits,
       act, act_shared, yexp, yexp_shared, ent, row_tok, row_w, moves, blk_cnt, blk_off, brank,
-      pact, pact_shared, pyexp, pyexp_shared, pf_hdr, pf_list, pf_ent, total;
+      pact, pact_shared, pyexp, pyexp_shared, pf_hdr, pf_list, pf_ent, row_cpu, cpu_key, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -133,6 +138,8 @@ Layout make_layout(const Dims& d) {
   L.pf_hdr = take(I4 * HDR_WORDS);
   L.pf_list = take(I4 * (size_t)(11 * d.E + 1));
   L.pf_ent = take(sizeof(int) * 4 * (size_t)d.E);
+  L.row_cpu = take(I4 * (size_t)d.adec);
+  L.cpu_key = take(I4 * (size_t)d.umax);
   L.total = o;
   return L;
 }
@@ -179,6 +186,9 @@ Dev make_dev(void* ws, const Layout& L) {
   v.pf_hdr = (int*)(b + L.pf_hdr);
   v.pf_list = (int*)(b + L.pf_list);
   v.pf_ent = (int4*)(b + L.pf_ent);
+  v.row_cpu = (int*)(b + L.row_cpu);
+  v.cpu_key = (int*)(b + L.cpu_key);
+  v.mail = nullptr;
   return v;
 }
 
@@ -277,8 +287,59 @@ struct Profiler {
   }
 };
 
+// Host side of hybrid decode: a server thread polls the mailbox that the route kernel posts
+// to, computes the step's CPU experts with its thread team straight from the host pool, and
+// answers with the step value.  The GPU combine waits for the answer.
+struct HybridServer {
+  HybMail* mail = nullptr;   // host view (pinned, coherent)
+  void* mail_dev = nullptr;  // device view
+  const unsigned char* pool = nullptr;
+  Dims d{};
+  int threads = 1;
+  std::thread th;
+  std::atomic<bool> stop{false};
+  std::atomic<long long> served{0};
+
+  void serve(CpuTeam& team, std::vector<float>& partial) {
+    HybMail* m = mail;
+    const int T = m->T, q = m->q, layer = m->layer, H = d.H;
+    float* y = (float*)((unsigned char*)m + mail_y_offset(H));
+    const uint16_t* x = (const uint16_t*)((const unsigned char*)m + mail_x_offset());
+    std::memset(y, 0, sizeof(float) * (size_t)T * H);
+    const uint16_t* blobs[kMailRows];
+    for (int j = 0; j < q; ++j)
+      blobs[j] = (const uint16_t*)(pool + ((size_t)layer * d.E + m->exp[j]) * (size_t)d.S);
+    cpu_experts_ffn(team, blobs, q, m->row0, m->ntok, m->row_tok, m->row_w, H, d.I, x, T, y,
+                    partial.data());
+  }
+  void loop() {
+    CpuTeam team(threads);
+    std::vector<float> partial((size_t)threads * kDecodeMaxTokens * d.H);
+    long long last = __atomic_load_n(&mail->req, __ATOMIC_ACQUIRE);
+    unsigned spins = 0;
+    while (!stop.load(std::memory_order_acquire)) {
+      const long long r = __atomic_load_n(&mail->req, __ATOMIC_ACQUIRE);
+      if (r == last) {
+        if (++spins < 4096) {
+          _mm_pause();
+        } else {
+          spins = 0;
+          std::this_thread::yield();
+        }
+        continue;
+      }
+      serve(team, partial);
+      last = r;
+      __atomic_store_n(&mail->done, r, __ATOMIC_RELEASE);
+      served.fetch_add(1, std::memory_order_relaxed);
+    }
+  }
+};
+
 struct moe_cache_s {
   Profiler prof;
+  HybridServer* hyb = nullptr;  // hybrid decode server, or null
+  int split_bc = 0, split_bp = 0;
   moe_shape shape;
   Dims d;
   Layout L;
@@ -397,8 +458,21 @@ moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t ma
   return MOE_OK;
 }
 
+static void hybrid_stop(moe_cache c) {
+  if (!c->hyb) return;
+  (void)hipDeviceSynchronize();  // no combine may still be waiting for the server
+  c->hyb->stop.store(true, std::memory_order_release);
+  if (c->hyb->th.joinable()) c->hyb->th.join();
+  if (c->hyb->mail) (void)hipHostFree(c->hyb->mail);
+  delete c->hyb;
+  c->hyb = nullptr;
+  c->v.mail = nullptr;
+  c->split_bc = c->split_bp = 0;
+}
+
 moe_status moe_cache_destroy(moe_cache c) {
   if (!c) return MOE_E_INVALID;
+  hybrid_stop(c);
   (void)c->prof.harvest_all();
   c->prof.destroy();
   if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
@@ -440,7 +514,9 @@ static hipError_t route_launch(moe_cache c, int layer, const void* x, int T, con
   return c->prof.timed(Profiler::ROUTE, s, [&](hipEvent_t e0, hipEvent_t e1) {
     if (T > kDecodeMaxTokens)
       return launch_route_prefill(c->d, c->v, x, wr, idx, w, layer, T, s, e0, e1);
-    return launch_route_plan(c->d, c->v, x, wr, idx, w, layer, T, s, e0, e1);
+    const bool split = c->hyb != nullptr;
+    return launch_route_plan(c->d, c->v, x, wr, idx, w, layer, T, split ? c->split_bc : 0,
+                             split ? c->split_bp : 0, s, e0, e1);
   });
 }
 
@@ -506,6 +582,90 @@ moe_status moe_set_prefetch(moe_cache c, int32_t enable) {
   if (enable && c->d.nblk == 0) return MOE_E_INVALID;  // a handle for decode steps only
   if (c->state != State::Idle || c->pf_layer[0] >= 0 || c->pf_layer[1] >= 0) return MOE_E_BUSY;
   c->prefetch = enable;
+  return MOE_OK;
+}
+
+moe_status moe_set_hybrid(moe_cache c, int32_t b_cpu_mbps, int32_t b_pcie_mbps, int32_t threads) {
+  if (!c) return MOE_E_INVALID;
+  if (c->state != State::Idle) return MOE_E_BUSY;
+  if (b_cpu_mbps == 0) {
+    hybrid_stop(c);
+    return MOE_OK;
+  }
+  if (b_cpu_mbps < 0 || b_pcie_mbps < 0 || threads < 1 || threads > 256) return MOE_E_INVALID;
+  if (c->d.fmt != FMT_BF16) return MOE_E_INVALID;  // the CPU path is bf16 only
+  if (c->hyb && c->hyb->threads != threads) hybrid_stop(c);
+  if (!c->hyb) {
+    HybridServer* h = new (std::nothrow) HybridServer();
+    if (!h) return MOE_E_NOMEM;
+    void* p = nullptr;
+    const size_t bytes = mail_bytes(c->d.H);
+    if (hipHostMalloc(&p, bytes, hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      delete h;
+      return MOE_E_NOMEM;
+    }
+    void* pd = nullptr;
+    if (hipHostGetDevicePointer(&pd, p, 0) != hipSuccess || !pd) {
+      (void)hipGetLastError();
+      (void)hipHostFree(p);
+      delete h;
+      return MOE_E_NOMEM;
+    }
+    std::memset(p, 0, bytes);
+    h->mail = (HybMail*)p;
+    h->mail->req = -1;
+    h->mail->done = -1;
+    h->mail_dev = pd;
+    h->pool = (const unsigned char*)c->host_pool;
+    h->d = c->d;
+    h->threads = threads;
+    h->th = std::thread([h] { h->loop(); });
+    c->hyb = h;
+    c->v.mail = (HybMail*)pd;
+  }
+  c->split_bc = b_cpu_mbps;
+  c->split_bp = b_pcie_mbps;
+  return MOE_OK;
+}
+
+moe_status moe_cpu_expert_ffn(const moe_shape* shape, const void* blob, const void* x, int32_t T,
+                              const float* w, float* y, int32_t threads) {
+  if (!shape_ok(shape) || shape->wfmt != MOE_FMT_BF16) return MOE_E_INVALID;
+  if (!blob || !x || !w || !y || T < 1 || T > kDecodeMaxTokens) return MOE_E_INVALID;
+  if (threads < 1 || threads > 256) return MOE_E_INVALID;
+  CpuTeam team(threads);
+  std::vector<float> partial((size_t)threads * T * shape->hidden);
+  int row_tok[kDecodeMaxTokens];
+  for (int t = 0; t < T; ++t) row_tok[t] = t;
+  const int row0 = 0, ntok = T;
+  const uint16_t* b = (const uint16_t*)blob;
+  cpu_experts_ffn(team, &b, 1, &row0, &ntok, row_tok, w, shape->hidden, shape->inter,
+                  (const uint16_t*)x, T, y, partial.data());
+  return MOE_OK;
+}
+
+moe_status moe_cpu_expert_rate(const moe_shape* shape, const void* pool, int32_t n_blobs,
+                               int32_t threads, int32_t reps, double* gbps) {
+  if (!shape_ok(shape) || shape->wfmt != MOE_FMT_BF16 || !pool || !gbps) return MOE_E_INVALID;
+  if (n_blobs < 1 || threads < 1 || threads > 256 || reps < 1) return MOE_E_INVALID;
+  const int H = shape->hidden, I = shape->inter;
+  CpuTeam team(threads);
+  std::vector<float> partial((size_t)threads * H), y(H);
+  std::vector<uint16_t> x(H, (uint16_t)0x3c00);  // 2^-7 in bf16
+  const int row_tok = 0, row0 = 0, ntok = 1;
+  const float w = 1.0f;
+  auto one = [&](int b) {
+    const uint16_t* blob = (const uint16_t*)((const unsigned char*)pool + (size_t)b * shape->blob_bytes);
+    cpu_experts_ffn(team, &blob, 1, &row0, &ntok, &row_tok, &w, H, I, x.data(), 1, y.data(),
+                    partial.data());
+  };
+  one(0);
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int r = 0; r < reps; ++r)
+    for (int b = 0; b < n_blobs; ++b) one(b);
+  const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  *gbps = (double)reps * n_blobs * (double)shape->blob_bytes / dt / 1e9;
   return MOE_OK;
 }
 
@@ -644,6 +804,7 @@ moe_status moe_cache_snapshot(moe_cache c, int32_t* key_of, int32_t* stamp, int3
   if (step) *step = (int64_t)(uint32_t)ctrl[CTRL_STEP_LO] | ((int64_t)ctrl[CTRL_STEP_HI] << 32);
   if (capacity) *capacity = ctrl[CTRL_C];
   if (ctrl[CTRL_ERR] & ERR_CAPACITY) return MOE_E_CAPACITY;
+  if (ctrl[CTRL_ERR] & ERR_HYBRID) return MOE_E_HYBRID;
   return MOE_OK;
 }
 
@@ -657,6 +818,7 @@ moe_status moe_plan_read(moe_cache c, moe_plan_host* o) {
   o->n_unique = nu;
   o->n_hit = hdr[HDR_NHIT];
   o->n_miss = nm;
+  o->n_cpu = hdr[HDR_NCPU];
   o->layer = hdr[HDR_LAYER];
   o->step = (int64_t)(uint32_t)hdr[HDR_STEP_LO] | ((int64_t)hdr[HDR_STEP_HI] << 32);
   std::vector<int> hit(nu > 0 ? nu : 1);
@@ -671,6 +833,7 @@ moe_status moe_plan_read(moe_cache c, moe_plan_host* o) {
   cp(o->miss_victim, c->v.miss_victim, 4 * (size_t)nm);
   cp(o->count, c->v.count, 4 * (size_t)nu);
   cp(o->perm, c->v.perm, 4 * (size_t)T * c->d.K);
+  cp(o->cpu_key, c->v.cpu_key, 4 * (size_t)o->n_cpu);
   if (e != hipSuccess) return hip_fail(c, e);
   if (o->hit)
     for (int i = 0; i < nu; ++i) o->hit[i] = (uint8_t)hit[i];
@@ -687,6 +850,11 @@ moe_status moe_stats(moe_cache c, moe_counters* out) {
   out->hits = (int64_t)s[STAT_HITS];
   out->misses = (int64_t)s[STAT_MISSES];
   out->bytes_filled = (int64_t)s[STAT_BYTES];
+  out->cpu_misses = (int64_t)s[STAT_CPU];
+  int ctrl[CTRL_WORDS];
+  e = hipMemcpy(ctrl, c->v.ctrl, sizeof(ctrl), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  if (ctrl[CTRL_ERR] & ERR_HYBRID) return MOE_E_HYBRID;
   return MOE_OK;
 }
 
@@ -733,6 +901,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_E_BUSY: return "a step is in flight";
     case MOE_E_HIP: return "HIP runtime error";
     case MOE_E_NOMEM: return "pinned host memory unavailable";
+    case MOE_E_HYBRID: return "hybrid decode: the host did not answer a step in time";
     default: return "unknown status";
   }
 }

@@ -594,22 +594,45 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
 
 
 // ---------------------------------------------------------------- combine role
-// y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + sum_rs yexp_shared[t][rs] ), in that fixed
-// order.  Every partial of a chunk is loaded before any is added (one memory latency per
-// chunk of CH partials).
+// y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + y_cpu[t] + sum_rs yexp_shared[t][rs] ), in
+// that fixed order; the routed sum skips the rows whose expert the CPU computed (hybrid
+// decode), and y_cpu[t] (their weighted sum, from the host mailbox) is added once the host
+// has answered this step.  Every partial of a chunk is loaded before any is added (one
+// memory latency per chunk of CH partials).
+constexpr long long kHybridSpin = 1ll << 23;  // ~2 s of polling before giving up (ERR_HYBRID)
+
 __device__ void combine_role(const FfnArgs& a, int cblk) {
   const Dims& d = a.d;
   const Dev& v = a.v;
   const int per_tok = (d.H + FT - 1) / FT;
   const int t = cblk / per_tok;
   const int c = (cblk % per_tok) * FT + threadIdx.x;
-  __shared__ int s_pos[32];
-  if ((int)threadIdx.x < d.K) s_pos[threadIdx.x] = v.inv_pos[t * d.K + threadIdx.x];
+  __shared__ int s_pos[32], s_cpu[32];
+  __shared__ int s_ncpu, s_ok;
+  if (threadIdx.x == 0) s_ncpu = v.hdr[HDR_NCPU];
+  __syncthreads();
+  const int ncpu = s_ncpu;
+  if ((int)threadIdx.x < d.K) {
+    const int pos = v.inv_pos[t * d.K + threadIdx.x];
+    s_pos[threadIdx.x] = pos;
+    s_cpu[threadIdx.x] = ncpu > 0 ? v.row_cpu[pos] : 0;
+  }
+  if (ncpu > 0 && threadIdx.x == 0) {
+    // wait for the host's answer to this step (bounded: an absent server sets ERR_HYBRID)
+    const long long step =
+        (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
+    long long it = 0;
+    while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step &&
+           ++it < kHybridSpin)
+      __builtin_amdgcn_s_sleep(8);
+    s_ok = it < kHybridSpin;
+    if (!s_ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
+  }
   __syncthreads();
   if (c >= d.H) return;
   constexpr int CH = 32;
   const int RS = d.RS, nrouted = d.K * RS, nall = nrouted + (d.has_shared ? RS : 0);
-  float s = 0.f;
+  float sr = 0.f, ss = 0.f;
   for (int base = 0; base < nall; base += CH) {
     float pv[CH];
 #pragma unroll
@@ -622,10 +645,21 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
       pv[q] = p[c];
     }
 #pragma unroll
-    for (int q = 0; q < CH; ++q)
-      if (base + q < nall) s += pv[q];
+    for (int q = 0; q < CH; ++q) {
+      const int i = base + q;
+      if (i < nrouted) {
+        if (!s_cpu[i / RS]) sr += pv[q];
+      } else if (i < nall) {
+        ss += pv[q];
+      }
+    }
   }
-  a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
+  float s = sr;
+  if (ncpu > 0 && s_ok) {
+    const float* yc = (const float*)((const unsigned char*)v.mail + mail_y_offset(d.H));
+    s += __hip_atomic_load(yc + (size_t)t * d.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s + ss);
 }
 
 template <int FMT>

@@ -35,9 +35,10 @@ enum : int {
   HDR_T = 4,
   HDR_STEP_LO = 5,
   HDR_STEP_HI = 6,
+  HDR_NCPU = 7,  // misses computed in place by the CPU (hybrid decode)
   HDR_WORDS = 16
 };
-enum : int { ERR_CAPACITY = 1 };
+enum : int { ERR_CAPACITY = 1, ERR_HYBRID = 2 };
 constexpr int kMaxSlots = 4096;  // most cache slots a handle supports (LDS-resident LRU)
 
 // Launch with optional timing events taken by the dispatch itself (start/end of the kernel,
@@ -58,6 +59,7 @@ enum : int {
   STAT_BYTES = 3,
   STAT_FFN_BYTES = 4,
   STAT_TIMED_BLOB_BYTES = 5,  // blobs read by gate/up launches bracketed by timing events
+  STAT_CPU = 6,               // misses computed in place by the CPU
   STAT_WORDS = 8
 };
 
@@ -76,6 +78,34 @@ struct Dims {
   int RS;            // row splits of the decode down projection
   long long S;       // blob bytes
 };
+
+// Hybrid decode mailbox in pinned, coherent host memory (one request in flight at a time).
+// The route kernel posts a request when it sends q > 0 misses of a step to the CPU: the CPU
+// experts, their rows (token, routing weight) and the step's activations, then `req` = the
+// step counter value.  The host server computes y_cpu[t] = sum over the CPU experts of
+// w * FFN_e(x_t), then sets `done` = req; the combine kernel waits for it.
+constexpr int kMailRows = 128;  // kDecodeMaxTokens * the largest top_k (16)
+struct HybMail {
+  long long req;
+  int layer, T, q, K;
+  int pad0[26];
+  int exp[kMailRows];    // CPU experts, ascending
+  int ntok[kMailRows];   // rows of each
+  int row0[kMailRows];   // first expert-sorted row of each
+  int row_tok[kMailRows];
+  float row_w[kMailRows];
+  long long done;        // own 128-byte line
+  int pad1[30];
+};
+static_assert(sizeof(HybMail) % 128 == 0, "mailbox lines");
+static_assert(__builtin_offsetof(HybMail, done) % 128 == 0, "done on its own line");
+__host__ __device__ inline size_t mail_x_offset() { return (sizeof(HybMail) + 127) & ~(size_t)127; }
+__host__ __device__ inline size_t mail_y_offset(int H) {
+  return mail_x_offset() + (((size_t)kDecodeMaxTokens * H * 2 + 127) & ~(size_t)127);
+}
+__host__ __device__ inline size_t mail_bytes(int H) {
+  return mail_y_offset(H) + (size_t)kDecodeMaxTokens * H * 4;
+}
 
 struct Dev {
   int* key_of;
@@ -120,6 +150,9 @@ struct Dev {
   int* pf_list;        // [11 * E + 1]: U, u_slot, u_hit, hit_list, miss_list, miss_key,
                        //   miss_slot, miss_victim, count, offset[E + 1]
   int4* pf_ent;        // [E]
+  int* row_cpu;        // [adec] 1: the row's expert is computed by the CPU (hybrid decode)
+  int* cpu_key;        // [umax] keys of the step's CPU misses, ascending expert
+  HybMail* mail;       // device view of the hybrid mailbox, or null
 };
 
 // Where a plan writes its outputs: the step plan or a prefetch plan.
@@ -136,17 +169,19 @@ struct PlanOut {
   int* offset;
   int4* ent;
   int* hdr;
+  int* cpu_key;  // keys of CPU misses (null: the plan never splits)
 };
 
 __host__ __device__ inline PlanOut step_plan_out(const Dev& v) {
   return PlanOut{v.U,         v.u_slot,      v.u_hit, v.hit_list, v.miss_list, v.miss_key,
-                 v.miss_slot, v.miss_victim, v.count, v.offset,   v.ent,       v.hdr};
+                 v.miss_slot, v.miss_victim, v.count, v.offset,   v.ent,       v.hdr,
+                 v.cpu_key};
 }
 
 __host__ __device__ inline PlanOut prefetch_plan_out(const Dev& v, int E) {
   int* b = v.pf_list;
   return PlanOut{b,         b + E,     b + 2 * E, b + 3 * E, b + 4 * E, b + 5 * E,
-                 b + 6 * E, b + 7 * E, b + 8 * E, b + 9 * E, v.pf_ent,  v.pf_hdr};
+                 b + 6 * E, b + 7 * E, b + 8 * E, b + 9 * E, v.pf_ent,  v.pf_hdr, nullptr};
 }
 
 constexpr int kMaxFillGroups = 64;

@@ -107,7 +107,25 @@ struct PlanTmp {
   uint64_t tmp64[8];
   int g;
   int err;
+  int nfill, ncpu;  // misses filled / computed by the CPU (set by plan_cache)
 };
+
+// Hybrid decode: how many of m misses the CPU computes in place.  Serving q misses on the
+// CPU (expert-weight rate bc) and m - q by fills (PCIe rate bp, both MB/s) finishes at
+// max((m - q) / bp, q / bc); q minimises it, the smaller q on a tie.  The makespan falls
+// while q is below the equal-finish point m*bc/(bc+bp) and rises after it, so the
+// minimiser is that point's floor or the next integer; exact in integers.
+// (FreeToken paper summary: q is a closed-form split by measured bandwidth, derived in the
+// fused routing kernel.)
+__host__ __device__ inline int miss_split(int m, int bc, int bp) {
+  if (m <= 0 || bc <= 0) return 0;
+  const long long q0 = (long long)m * bc / ((long long)bc + (long long)bp);
+  if (q0 >= m) return m;
+  const long long a0 = (m - q0) * (long long)bc, b0 = q0 * (long long)bp;
+  const long long a1 = (m - q0 - 1) * (long long)bc, b1 = (q0 + 1) * (long long)bp;
+  const long long t0 = a0 > b0 ? a0 : b0, t1 = a1 > b1 ? a1 : b1;
+  return (int)(t1 < t0 ? q0 + 1 : q0);
+}
 
 // Cache state the plan reads, loaded once at its start.
 struct PlanState {
@@ -170,11 +188,14 @@ __device__ inline int plan_dedup(const Dims& d, const PlanOut& o, PlanLds& s, Pl
 
 // Classification, LRU victims, slot-table update, entry table, header and counters, written
 // to `o`.  The slots prot[0 .. n_prot) are never victims (a prefetch protects the slots of the
-// step before it).  Returns false (after recording the error and an empty plan) when fewer
-// slots can be evicted than there are misses.
+// step before it).  With split rates (bc > 0, decode only) the last q = miss_split(m) misses
+// in ascending expert id are computed by the CPU: no slot, no eviction, no stamp; the
+// header's miss count is then the filled misses only.  Returns false (after recording the
+// error and an empty plan) when fewer slots can be evicted than there are misses to fill.
 __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o, int layer,
                                   int T, int nU, PlanLds& s, const PlanState& ps, PlanTmp& pt,
-                                  const int* prot = nullptr, int n_prot = 0) {
+                                  const int* prot = nullptr, int n_prot = 0, int split_bc = 0,
+                                  int split_bp = 0) {
   const int E = d.E, umax = d.umax;
   for (int u = threadIdx.x; u < nU; u += RT) {
     const int sl = s.srow[s.U[u]];
@@ -189,13 +210,15 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
         s.hitl[pos] = u;
       },
       pt.tmp);
-  const int nMiss = block_compact(
+  const int nAllMiss = block_compact(
       nU, [&](int u) { return s.hit[u] == 0; },
       [&](int u, int pos) {
         s.miss[pos] = u;
         o.miss_list[pos] = u;
       },
       pt.tmp);
+  const int nCpu = miss_split(nAllMiss, split_bc, split_bp);
+  const int nMiss = nAllMiss - nCpu;  // misses filled into slots: the first nMiss of the list
 
   // LRU victims: the `need` smallest (stamp, key) among occupied slots not used this step,
   // found in rounds of "oldest remaining stamp" (one round per distinct stamp taken: a
@@ -264,6 +287,9 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
       o.hdr[HDR_NU] = 0;
       o.hdr[HDR_NHIT] = 0;
       o.hdr[HDR_NMISS] = 0;
+      o.hdr[HDR_NCPU] = 0;
+      pt.nfill = 0;
+      pt.ncpu = 0;
     }
     return false;
   }
@@ -291,12 +317,14 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
   }
   __syncthreads();
   for (int u = threadIdx.x; u < nU; u += RT) {
-    v.stamp[s.uslot[u]] = (int)ps.step;
+    if (s.uslot[u] >= 0) v.stamp[s.uslot[u]] = (int)ps.step;  // CPU misses hold no slot
     o.u_slot[u] = s.uslot[u];
     o.u_hit[u] = s.hit[u];
   }
-  // FFN entry table: hits first, then misses in ascending expert id (the fill order)
-  for (int g = threadIdx.x; g < nU; g += RT) {
+  if (o.cpu_key)
+    for (int j = threadIdx.x; j < nCpu; j += RT) o.cpu_key[j] = layer * E + s.U[s.miss[nMiss + j]];
+  // FFN entry table: hits first, then filled misses in ascending expert id (the fill order)
+  for (int g = threadIdx.x; g < nHit + nMiss; g += RT) {
     const int miss = g < nHit ? -1 : g - nHit;
     const int u = miss < 0 ? s.hitl[g] : s.miss[miss];
     o.ent[g] = make_int4(s.uslot[u], s.cnt[s.U[u]], s.off[u], miss);
@@ -307,6 +335,7 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
     o.hdr[HDR_NU] = nU;
     o.hdr[HDR_NHIT] = nHit;
     o.hdr[HDR_NMISS] = nMiss;
+    o.hdr[HDR_NCPU] = nCpu;
     o.hdr[HDR_LAYER] = layer;
     o.hdr[HDR_T] = T;
     o.hdr[HDR_STEP_LO] = (int)(ps.step & 0xffffffff);
@@ -316,8 +345,11 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
     v.ctrl[CTRL_STEP_HI] = (int)(ns >> 32);
     v.stats[STAT_STEPS] += 1;
     v.stats[STAT_HITS] += (unsigned long long)nHit;
-    v.stats[STAT_MISSES] += (unsigned long long)nMiss;
+    v.stats[STAT_MISSES] += (unsigned long long)nAllMiss;
+    v.stats[STAT_CPU] += (unsigned long long)nCpu;
     v.stats[STAT_BYTES] += (unsigned long long)nMiss * (unsigned long long)d.S;
+    pt.nfill = nMiss;
+    pt.ncpu = nCpu;
   }
   return true;
 }

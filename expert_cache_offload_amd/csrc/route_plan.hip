@@ -36,6 +36,7 @@ struct RouteArgs {
   float* out_w;        // [T][K] or null
   int layer;
   int T;
+  int split_bc, split_bp;  // hybrid decode: CPU expert rate and PCIe fill rate (MB/s), 0: off
 };
 
 __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
@@ -123,7 +124,9 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   double* s_z = (double*)p;     p += sizeof(double) * (size_t)kDecodeMaxTokens * E;
   int* s_tk_idx = (int*)p;      p += sizeof(int) * d.adec;
   float* s_tk_w = (float*)p;    p += sizeof(float) * d.adec;
-  double* s_tk_z = (double*)p;
+  double* s_tk_z = (double*)p; p += sizeof(double) * d.adec;
+  int* s_rt = (int*)p;          p += sizeof(int) * d.adec;   // token of each sorted row
+  float* s_rw = (float*)p;                                   // routing weight of each row
   __shared__ PlanTmp pt;
   PlanState ps;
 
@@ -184,8 +187,47 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     v.inv_pos[i] = pos;
     v.row_tok[pos] = i / K;
     v.row_w[pos] = s_tk_w[i];
+    s_rt[pos] = i / K;
+    s_rw[pos] = s_tk_w[i];
   }
-  plan_cache(d, v, o, layer, T, nU, s, ps, pt);
+  plan_cache(d, v, o, layer, T, nU, s, ps, pt, nullptr, 0, a.split_bc, a.split_bp);
+  if (a.split_bc > 0) {
+    // hybrid decode: flag the rows of the CPU experts (the combine skips them) and post the
+    // request to the host: CPU experts, the step's rows, the activations, then the step value
+    __syncthreads();
+    const int q = pt.ncpu, nfill = pt.nfill;
+    for (int r = threadIdx.x; r < A; r += RT) v.row_cpu[r] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < q; j += RT) {
+      const int u = s.miss[nfill + j];
+      for (int r = s.off[u]; r < s.off[u + 1]; ++r) v.row_cpu[r] = 1;
+    }
+    if (q > 0 && wave == 0) {
+      HybMail* m = v.mail;
+      for (int j = lane; j < q; j += 64) {
+        const int u = s.miss[nfill + j];
+        m->exp[j] = s.U[u];
+        m->ntok[j] = s.off[u + 1] - s.off[u];
+        m->row0[j] = s.off[u];
+      }
+      for (int r = lane; r < A; r += 64) {
+        m->row_tok[r] = s_rt[r];
+        m->row_w[r] = s_rw[r];
+      }
+      if (lane == 0) {
+        m->layer = layer;
+        m->T = T;
+        m->q = q;
+        m->K = K;
+      }
+      uint4* mx = (uint4*)((unsigned char*)m + mail_x_offset());
+      const uint4* xs = (const uint4*)a.x;
+      for (int i = lane; i < T * H / 8; i += 64) mx[i] = xs[i];
+      __threadfence_system();
+      if (lane == 0)
+        __hip_atomic_store(&m->req, ps.step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
   if (threadIdx.x == 0)
     __hip_atomic_store(&v.ctrl[CTRL_TICKET], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -194,16 +236,23 @@ size_t route_plan_lds_bytes(const Dims& d) {
   size_t b = plan_lds_bytes(d);
   b += sizeof(double) * (size_t)kDecodeMaxTokens * d.E;
   b += (sizeof(int) + sizeof(float) + sizeof(double)) * (size_t)d.adec;
+  b += (sizeof(int) + sizeof(float)) * (size_t)d.adec;
   return (b + 15) & ~(size_t)15;
 }
 
 hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const void* wr,
-                             int* out_idx, float* out_w, int layer, int T, hipStream_t s,
-                             hipEvent_t e0, hipEvent_t e1) {
-  RouteArgs a{d, v, (const uint16_t*)x, (const uint16_t*)wr, out_idx, out_w, layer, T};
+                             int* out_idx, float* out_w, int layer, int T, int split_bc,
+                             int split_bp, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  RouteArgs a{d, v, (const uint16_t*)x, (const uint16_t*)wr, out_idx, out_w, layer, T,
+              split_bc, split_bp};
   int grid = (d.E + (RT / 64) - 1) / (RT / 64);
-  return launch_timed(route_plan_kernel, dim3(grid), dim3(RT), route_plan_lds_bytes(d), s, e0, e1,
-                      a);
+  const size_t lds = route_plan_lds_bytes(d);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)route_plan_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  return launch_timed(route_plan_kernel, dim3(grid), dim3(RT), lds, s, e0, e1, a);
 }
 
 }  // namespace moe

@@ -18,7 +18,7 @@ import moe_inputs as mi
 from . import (make_shape, moe_cache_create, moe_cache_destroy, moe_cache_resize,
                moe_cache_snapshot, moe_expert_ffn, moe_fill_misses, moe_host_pool_alloc,
                moe_host_pool_free, moe_layer_step, moe_plan_read, moe_route_classify,
-               moe_set_prefetch, moe_stats, moe_workspace_bytes)
+               moe_set_hybrid, moe_set_prefetch, moe_stats, moe_workspace_bytes)
 
 
 def pinned_view(addr: int, nbytes: int) -> np.ndarray:
@@ -117,10 +117,18 @@ class Workbench:
         self.sync()
         if getattr(self, "prefetch", False):
             moe_set_prefetch(self.handle, True)
+        if getattr(self, "hybrid", None):
+            moe_set_hybrid(self.handle, *self.hybrid)
 
     def set_prefetch(self, enable: bool) -> None:
         self.prefetch = bool(enable)
         moe_set_prefetch(self.handle, self.prefetch)
+
+    def set_hybrid(self, b_cpu_mbps: int, b_pcie_mbps: int = 0, threads: int = 8) -> None:
+        """Split decode misses between fills and the CPU (b_cpu_mbps 0: off)."""
+        self.sync()
+        self.hybrid = (int(b_cpu_mbps), int(b_pcie_mbps), int(threads)) if b_cpu_mbps else None
+        moe_set_hybrid(self.handle, int(b_cpu_mbps), int(b_pcie_mbps), int(threads))
 
     def sync(self) -> None:
         torch.cuda.synchronize(self.dev)

@@ -72,6 +72,7 @@ typedef int32_t moe_status;
 #define MOE_E_BUSY (-3)     /* resize or snapshot while a step is in flight */
 #define MOE_E_HIP (-4)      /* a HIP runtime call failed; see moe_last_hip_error */
 #define MOE_E_NOMEM (-5)    /* pinned host allocation failed */
+#define MOE_E_HYBRID (-6)   /* hybrid decode: the host did not answer a step within ~2 s */
 
 #define MOE_FMT_BF16 0
 #define MOE_FMT_FP8_E4M3_K128 1
@@ -95,6 +96,7 @@ typedef struct {
 typedef struct {
   int32_t n_unique, n_hit, n_miss, layer;
   int64_t step;
+  int32_t n_cpu, pad_;  /* misses computed in place by the CPU (hybrid decode) */
   int32_t* unique;    /* [n_unique] distinct experts, ascending */
   int32_t* slot;      /* [n_unique] cache slot of each, after the step */
   uint8_t* hit;       /* [n_unique] 1 = was cached before the step */
@@ -103,10 +105,12 @@ typedef struct {
   int32_t* miss_victim; /* [n_miss] evicted key, or -1 for a free slot */
   int32_t* count;     /* [n_unique] assignments per distinct expert */
   int32_t* perm;      /* [T*top_k] assignment ids t*top_k+j grouped by expert, ascending t */
+  int32_t* cpu_key;   /* [n_cpu] keys of the CPU misses, ascending expert (may be NULL) */
 } moe_plan_host;      /* caller-owned arrays sized for min(max_tokens*top_k, experts) / T*top_k */
 
 typedef struct {
   int64_t steps, hits, misses, bytes_filled;
+  int64_t cpu_misses; /* misses computed in place by the CPU (hybrid decode) */
 } moe_counters;
 
 /* Bytes of one expert blob, or -1 for an unsupported shape. */
@@ -200,6 +204,39 @@ moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int32_t* stamp,
  * while a step or a prefetch is in flight (moe_cache_resize is MOE_E_BUSY too until the
  * prefetched layer's step has run). */
 moe_status moe_set_prefetch(moe_cache cache, int32_t enable);
+
+/* Hybrid decode: split each decode step's misses between PCIe fills and in-place CPU
+ * compute (FreeToken paper summary, agihunt.info / arXiv 2608.16157: problem, execution-layer
+ * and last paragraphs - a miss is either moved or computed by the CPU, the split q is a
+ * closed form of measured bandwidths derived inside the fused routing kernel; the CPU path
+ * exists for bf16 weights only, "FreeToken: az VRAM ile büyük MoE modelleri", "Tuzaklar").
+ * b_cpu_mbps: the CPU's expert-weight rate, b_pcie_mbps: the fill rate, both MB/s; a step
+ * with m misses (T <= 8) sends the last q of them (ascending expert id) to the CPU, q the
+ * integer minimising max((m - q) / b_pcie, q / b_cpu), the smaller on a tie.  CPU misses take
+ * no slot, evict nothing and are not stamped.  The route kernel posts them to a pinned
+ * mailbox that a server thread of this handle polls; `threads` host threads (the server
+ * and its team, which spin while idle) compute them from the host pool, and the combine
+ * kernel adds their sum once the host has answered (after ~2 s without an answer it gives
+ * up and the next moe_stats / moe_cache_snapshot returns MOE_E_HYBRID).  b_cpu_mbps = 0
+ * turns the split off (and stops the threads).  bf16 weights only (MOE_E_INVALID
+ * otherwise); MOE_E_BUSY while a step is in flight; MOE_E_NOMEM if the mailbox cannot be
+ * pinned.  Choosing the mode is the caller's: the pages switch to the split only when the
+ * CPU expert rate is at least 2.0x the offload rate. */
+moe_status moe_set_hybrid(moe_cache cache, int32_t b_cpu_mbps, int32_t b_pcie_mbps,
+                          int32_t threads);
+
+/* The CPU expert FFN of the hybrid path, on host buffers (no GPU involved): for t < T,
+ * y[t][:] += w[t] * FFN(x[t]) with the bf16 expert blob `blob` (shape's layout), x [T][hidden]
+ * bf16, y [T][hidden] fp32, using `threads` host threads.  T in 1..8.  MOE_E_INVALID for a
+ * non-bf16 shape or bad arguments. */
+moe_status moe_cpu_expert_ffn(const moe_shape* shape, const void* blob, const void* x, int32_t T,
+                              const float* w, float* y, int32_t threads);
+
+/* Measured expert-weight rate of the CPU path: one token through each of the first n_blobs
+ * blobs of `pool` (host memory, shape's layout), `reps` times, with `threads` host threads;
+ * *gbps = blob bytes processed / wall time / 1e9 (the CPU rate of the mode choice). */
+moe_status moe_cpu_expert_rate(const moe_shape* shape, const void* pool, int32_t n_blobs,
+                               int32_t threads, int32_t reps, double* gbps);
 
 /* Synchronous copy of the last plan (see moe_plan_host). */
 moe_status moe_plan_read(moe_cache cache, moe_plan_host* out);

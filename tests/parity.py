@@ -38,6 +38,7 @@ def compare_step(wb, ref, ctx: str, check_state: bool = True, check_y: bool = Tr
     assert list(p["slot"]) == rec.slot, f"{ctx}: slot {p['slot']} vs {rec.slot}"
     got_m = list(zip(p["miss_key"].tolist(), p["miss_slot"].tolist(), p["miss_victim"].tolist()))
     assert got_m == [tuple(m) for m in rec.misses], f"{ctx}: misses {got_m} vs {rec.misses}"
+    assert list(p["cpu_key"]) == list(rec.cpu), f"{ctx}: cpu misses {p['cpu_key']} vs {rec.cpu}"
     assert list(p["count"]) == [int(ref.count[e]) for e in rec.U], f"{ctx}: counts"
     A = wb.T * wl.top_k
     assert np.array_equal(p["perm"][:A], ref.perm), f"{ctx}: perm"

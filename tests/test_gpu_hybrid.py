@@ -1,0 +1,84 @@
+"""GPU parity of hybrid decode: each step's misses split between PCIe fills and in-place CPU
+compute (the route kernel derives q, the host server computes the CPU experts from the pinned
+pool, the combine adds them), against the float64 oracle with the same integer rates.
+
+Integer results - including which misses went to the CPU - and the cache state are compared
+bit-exactly every step; layer outputs within the bf16 relative-L2 tolerance per token."""
+import sys
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+from parity import compare_step
+
+pytestmark = pytest.mark.gpu
+
+RATES = (124_500, 56_000)  # CPU expert rate, PCIe fill rate (MB/s): 1-3 misses mostly to the CPU
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(wl, n_tok, groups, rates=RATES, threads=6, switch_off_at=None):
+    from expert_cache_offload_amd.runner import Workbench
+    from oracle.step import Oracle
+    with Workbench(wl, groups=groups) as wb:
+        wb.set_hybrid(rates[0], rates[1], threads)
+        orc = Oracle(wl, wb.pool, wb.router_np, split=rates)
+        worst, n_cpu, n_miss = 0.0, 0, 0
+        for t in range(n_tok):
+            if switch_off_at is not None and t == switch_off_at:
+                wb.set_hybrid(0)
+                orc.split = None
+            for l in range(wl.layers):
+                wb.step(t, l)
+                ref = orc.layer_step(t, l, wb.acts_np[t, l], True)
+                err = compare_step(wb, ref, f"{wl.name} hybrid t={t} l={l}")
+                worst = max(worst, err)
+                n_cpu += len(ref.rec.cpu)
+                n_miss += len(ref.rec.cpu) + len(ref.rec.misses)
+        st = wb.stats()
+        assert st["cpu_misses"] == n_cpu and st["misses"] == n_miss
+        return worst, n_cpu, n_miss
+
+
+def test_hybrid_tiny_every_step():
+    wl = mi.WORKLOADS["tiny"].with_steps(48)
+    worst, n_cpu, n_miss = _run(wl, wl.token_steps, groups=0, threads=3)
+    _log(f"tiny hybrid: max rel-L2 {worst:.2e}, {n_cpu} of {n_miss} misses on the CPU")
+    assert n_cpu > 0
+
+
+@pytest.mark.parametrize("groups", [0, 2])
+def test_hybrid_35b_shape(groups):
+    wl = mi.WORKLOADS["qwen35b_decode"].with_layers(4).with_steps(16)
+    worst, n_cpu, n_miss = _run(wl, wl.token_steps, groups=groups)
+    _log(f"35B hybrid groups={groups}: max rel-L2 {worst:.2e}, {n_cpu} of {n_miss} misses on the CPU")
+    assert n_cpu > 0 and n_cpu < n_miss
+
+
+def test_hybrid_eight_streams_then_off():
+    wl = mi.WORKLOADS["qwen35b_decode_b8"].with_layers(3).with_steps(8)
+    worst, n_cpu, n_miss = _run(wl, wl.token_steps, groups=0, threads=8, switch_off_at=5)
+    _log(f"8 streams hybrid: max rel-L2 {worst:.2e}, {n_cpu} of {n_miss} misses on the CPU")
+    assert n_cpu > 0
+
+
+def test_hybrid_cpu_slower_than_pcie():
+    # CPU at 40 GB/s against 56: one miss is filled, two split one-one, five put two on the CPU
+    wl = mi.WORKLOADS["qwen35b_decode"].with_layers(2).with_steps(12)
+    worst, n_cpu, n_miss = _run(wl, wl.token_steps, groups=0, rates=(40_000, 56_000))
+    _log(f"35B hybrid, slow CPU: max rel-L2 {worst:.2e}, {n_cpu} of {n_miss} misses on the CPU")
+    assert 0 < n_cpu < n_miss
+
+
+def test_hybrid_rejects_non_bf16():
+    from expert_cache_offload_amd import MoeError
+    from expert_cache_offload_amd.runner import Workbench
+    wl = mi.WORKLOADS["dsv4_fp8_decode"].with_layers(1).with_steps(1)
+    with Workbench(wl, groups=0) as wb:
+        with pytest.raises(MoeError):
+            wb.set_hybrid(*RATES, 4)
