@@ -337,6 +337,11 @@ def main() -> None:
     ap.add_argument("--cpu-tokens", type=int, default=1, help="oracle sample (token steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events")
+    ap.add_argument("--mode", choices=("auto", "offload", "hybrid"), default="auto",
+                    help="decode misses: fill all (offload), split with the CPU (hybrid), or "
+                         "choose by the measured CPU/offload rate ratio against 2.0 (auto)")
+    ap.add_argument("--cpu-threads", type=int, default=12,
+                    help="host threads of the hybrid CPU expert path")
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
     args.warmup_given = "--warmup" in sys.argv
@@ -347,7 +352,8 @@ def main() -> None:
     import torch
 
     import moe_inputs as mi
-    from expert_cache_offload_amd import (PROF_ALL, PROF_GATE_UP, moe_profile_enable,
+    from expert_cache_offload_amd import (PROF_ALL, PROF_FILL, PROF_GATE_UP, choose_hybrid,
+                                          moe_cpu_expert_rate, moe_profile_enable,
                                           moe_profile_read)
     from expert_cache_offload_amd.runner import Workbench
 
@@ -377,15 +383,42 @@ def main() -> None:
         for l in range(L):
             wb.step(t, l)
 
-    for t in range(args.warmup):
-        if t == resize_at:
-            wb.sync()
-            wb.resize(wl.resize_capacity)
-        token(t)
-        if t % 16 == 15:
-            wb.sync()
-            print(f"[bench] warmup token {t}", file=sys.stderr, flush=True)
-    wb.sync()
+    def warm():
+        for t in range(args.warmup):
+            if t == resize_at:
+                wb.sync()
+                wb.resize(wl.resize_capacity)
+            token(t)
+            if t % 16 == 15:
+                wb.sync()
+                print(f"[bench] warmup token {t}", file=sys.stderr, flush=True)
+        wb.sync()
+
+    warm()
+    # mode choice (bf16 only has a CPU path): the fill kernel's rate over a few tokens of the
+    # offload run against the CPU expert path's rate on pool blobs, threshold 2.0x
+    hybrid = None
+    if args.mode != "offload" and wl.fmt != 0:
+        hybrid = {"mode": "offload", "note": "no CPU expert path for this weight format"}
+    if args.mode != "offload" and wl.fmt == 0:
+        moe_profile_enable(wb.handle, PROF_FILL)
+        for t in range(8):
+            token(t)
+        pf = moe_profile_read(wb.handle)
+        moe_profile_enable(wb.handle, 0)
+        pcie = pf["fill_bytes"] / (pf["fill"]["ms"] / 1e3) / 1e9 if pf["fill"]["ms"] else 0.0
+        cpu_rate = moe_cpu_expert_rate(wb.shape, wb.pool_addr, 48, args.cpu_threads, 2)
+        use = args.mode == "hybrid" or choose_hybrid(cpu_rate, pcie)
+        hybrid = {"mode": "hybrid" if use else "offload", "cpu_expert_GBps": round(cpu_rate, 2),
+                  "offload_GBps": round(pcie, 2), "ratio": round(cpu_rate / pcie, 3) if pcie else None,
+                  "threshold": 2.0, "cpu_threads": args.cpu_threads,
+                  "choice": "forced" if args.mode == "hybrid" else "measured"}
+        print(f"[bench] CPU expert path {cpu_rate:.1f} GB/s, fills {pcie:.1f} GB/s -> "
+              f"{hybrid['mode']}", file=sys.stderr, flush=True)
+        if use:
+            wb.set_hybrid(int(cpu_rate * 1000), int(pcie * 1000), args.cpu_threads)
+            wb.reset()  # from a cold cache again, now splitting misses
+            warm()
     st0 = wb.stats()
     if not args.no_profile:
         moe_profile_enable(wb.handle, PROF_GATE_UP, args.profile_every)
@@ -425,6 +458,22 @@ def main() -> None:
         moe_profile_enable(wb.handle, 0)
     hits = st1["hits"] - st0["hits"]
     misses = st1["misses"] - st0["misses"]
+    cpu_misses = st1["cpu_misses"] - st0["cpu_misses"]
+    if hybrid is not None and hybrid["mode"] == "hybrid":
+        # ablation: the same tokens with every miss filled, from a cold cache
+        wb.set_hybrid(0)
+        wb.reset()
+        warm()
+        n_ab = min(96, args.steps)
+        torch.cuda.synchronize()
+        a0 = time.perf_counter()
+        for t in range(args.warmup, args.warmup + n_ab):
+            token(t)
+        torch.cuda.synchronize()
+        hybrid["offload_tok_s"] = round(n_ab * wl.tokens_per_step / (time.perf_counter() - a0), 3)
+        hybrid["offload_tokens"] = n_ab
+        print(f"[bench] offload ablation {hybrid['offload_tok_s']:.2f} tok/s", file=sys.stderr,
+              flush=True)
     fill_bytes = st1["bytes_filled"] - st0["bytes_filled"]
     tokens = args.steps * wl.tokens_per_step
     tok_s = tokens / wall
@@ -514,6 +563,8 @@ def main() -> None:
         "fill": fill,
         "miss_rate": round(misses / max(1, hits + misses), 4),
         "misses_per_token": round(misses / max(1, tokens), 2),
+        "cpu_misses_per_token": round(cpu_misses / max(1, tokens), 2),
+        "hybrid": hybrid,
         **extra,
     }
     print(json.dumps(line), flush=True)

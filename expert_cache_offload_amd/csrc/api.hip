@@ -313,9 +313,11 @@ struct HybridServer {
                     partial.data());
   }
   void loop() {
+    // the mailbox starts with req = -1; a request may already be posted by the time this
+    // thread runs, so `last` is that initial value, never a fresh read
+    long long last = -1;
     CpuTeam team(threads);
     std::vector<float> partial((size_t)threads * kDecodeMaxTokens * d.H);
-    long long last = __atomic_load_n(&mail->req, __ATOMIC_ACQUIRE);
     unsigned spins = 0;
     while (!stop.load(std::memory_order_acquire)) {
       const long long r = __atomic_load_n(&mail->req, __ATOMIC_ACQUIRE);

@@ -26,8 +26,10 @@ def _run(wl, n_tok, groups, rates=RATES, threads=6, switch_off_at=None):
     from expert_cache_offload_amd.runner import Workbench
     from oracle.step import Oracle
     with Workbench(wl, groups=groups) as wb:
-        wb.set_hybrid(rates[0], rates[1], threads)
         orc = Oracle(wl, wb.pool, wb.router_np, split=rates)
+        # the first step follows at once: the request may be posted before the server thread
+        # has started
+        wb.set_hybrid(rates[0], rates[1], threads)
         worst, n_cpu, n_miss = 0.0, 0, 0
         for t in range(n_tok):
             if switch_off_at is not None and t == switch_off_at:
@@ -47,7 +49,7 @@ def _run(wl, n_tok, groups, rates=RATES, threads=6, switch_off_at=None):
 
 def test_hybrid_tiny_every_step():
     wl = mi.WORKLOADS["tiny"].with_steps(48)
-    worst, n_cpu, n_miss = _run(wl, wl.token_steps, groups=0, threads=3)
+    worst, n_cpu, n_miss = _run(wl, wl.token_steps, groups=0, threads=12)
     _log(f"tiny hybrid: max rel-L2 {worst:.2e}, {n_cpu} of {n_miss} misses on the CPU")
     assert n_cpu > 0
 
