@@ -166,9 +166,11 @@ def _ffn_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def _traffic_from_profile(name: str) -> float | None:
-    """HBM bytes per gate/up launch from a committed counter summary, if it was taken on the
-    current kernel source (its header line records the source hash)."""
+def _traffic_ratio_from_profile(name: str) -> float | None:
+    """HBM bytes per algorithmic byte of the gate/up kernel from a committed counter summary,
+    if it was taken on the current kernel source (its header line records the source hash).
+    The counters are taken with every launch streaming the same number of experts; the bench
+    scales the ratio by its own algorithmic bytes per launch."""
     here = os.path.dirname(os.path.abspath(__file__))
     p = os.path.join(here, "profiles", name)
     if not os.path.exists(p):
@@ -179,7 +181,7 @@ def _traffic_from_profile(name: str) -> float | None:
     for line in open(p):
         if line.startswith("ffn_source_sha256_16:") and line.split(":", 1)[1].strip() == h:
             src_ok = True
-        if line.startswith("hbm_bytes_per_launch:"):
+        if line.startswith("hbm_bytes_per_algorithmic_byte:"):
             val = float(line.split(":", 1)[1])
     return val if src_ok else None
 
@@ -342,6 +344,10 @@ def main() -> None:
                          "choose by the measured CPU/offload rate ratio against 2.0 (auto)")
     ap.add_argument("--cpu-threads", type=int, default=12,
                     help="host threads of the hybrid CPU expert path")
+    ap.add_argument("--hybrid-rates", default="",
+                    help="CPU,PCIe rates in MB/s: hybrid mode with these rates, no probe")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the offload run that follows a hybrid run")
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
     args.warmup_given = "--warmup" in sys.argv
@@ -400,7 +406,15 @@ def main() -> None:
     hybrid = None
     if args.mode != "offload" and wl.fmt != 0:
         hybrid = {"mode": "offload", "note": "no CPU expert path for this weight format"}
-    if args.mode != "offload" and wl.fmt == 0:
+    if args.hybrid_rates and wl.fmt == 0:
+        bc, bp = (int(v) for v in args.hybrid_rates.split(","))
+        hybrid = {"mode": "hybrid", "cpu_expert_GBps": bc / 1e3, "offload_GBps": bp / 1e3,
+                  "ratio": round(bc / bp, 3), "threshold": 2.0, "cpu_threads": args.cpu_threads,
+                  "choice": "given"}
+        wb.set_hybrid(bc, bp, args.cpu_threads)
+        wb.reset()
+        warm()
+    elif args.mode != "offload" and wl.fmt == 0:
         moe_profile_enable(wb.handle, PROF_FILL)
         for t in range(8):
             token(t)
@@ -459,7 +473,7 @@ def main() -> None:
     hits = st1["hits"] - st0["hits"]
     misses = st1["misses"] - st0["misses"]
     cpu_misses = st1["cpu_misses"] - st0["cpu_misses"]
-    if hybrid is not None and hybrid["mode"] == "hybrid":
+    if hybrid is not None and hybrid["mode"] == "hybrid" and not args.no_ablation:
         # ablation: the same tokens with every miss filled, from a cold cache
         wb.set_hybrid(0)
         wb.reset()
@@ -496,7 +510,8 @@ def main() -> None:
         gu_bytes = prof["gate_up_timed_bytes"]  # expert bytes the timed launches were given
         gu_s = gu["ms"] / 1e3
         achieved = gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0
-        traffic = _traffic_from_profile(f"ffn_gate_up_{wl.name}_pmc.txt")
+        ratio = _traffic_ratio_from_profile(f"ffn_gate_up_{wl.name}_pmc.txt")
+        traffic = round(ratio * gu_bytes / max(1, gu["launches"])) if ratio else None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": traffic, "kernel": "ffn_gate_up_kernel",
