@@ -89,6 +89,8 @@ _SIGS = {
     "moe_profile_enable": (_i32, [_vp, _i32, _i32]),
     "moe_set_prefetch": (_i32, [_vp, _i32]),
     "moe_set_hybrid": (_i32, [_vp, _i32, _i32, _i32]),
+    "moe_hybrid_read": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                               ctypes.POINTER(ctypes.c_double)]),
     "moe_cpu_expert_ffn": (_i32, [ctypes.POINTER(MoeShape), _vp, _vp, _i32, _vp, _vp, _i32]),
     "moe_cpu_expert_rate": (_i32, [ctypes.POINTER(MoeShape), _vp, _i32, _i32, _i32,
                                    ctypes.POINTER(ctypes.c_double)]),
@@ -241,6 +243,14 @@ def moe_set_hybrid(handle: int, b_cpu_mbps: int, b_pcie_mbps: int, threads: int)
     """Split decode misses between fills and in-place CPU compute (b_cpu_mbps 0: off)."""
     _check(_lib.moe_set_hybrid(handle, int(b_cpu_mbps), int(b_pcie_mbps), int(threads)),
            "moe_set_hybrid", handle)
+
+
+def moe_hybrid_read(handle: int) -> dict:
+    """Host-side counters of the hybrid server: requests, experts, busy seconds."""
+    r, e, b = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(_lib.moe_hybrid_read(handle, ctypes.byref(r), ctypes.byref(e), ctypes.byref(b)),
+           "moe_hybrid_read", handle)
+    return {"requests": int(r.value), "experts": int(e.value), "busy_s": float(b.value)}
 
 
 def moe_cpu_expert_ffn(shape: MoeShape, blob: int, x: int, T: int, w: int, y: int,

@@ -298,7 +298,9 @@ struct HybridServer {
   int threads = 1;
   std::thread th;
   std::atomic<bool> stop{false};
-  std::atomic<long long> served{0};
+  std::atomic<long long> served{0};   // requests answered
+  std::atomic<long long> experts{0};  // CPU experts computed
+  std::atomic<long long> busy_ns{0};  // time spent computing them
 
   void serve(CpuTeam& team, std::vector<float>& partial) {
     HybMail* m = mail;
@@ -330,9 +332,15 @@ struct HybridServer {
         }
         continue;
       }
+      const auto t0 = std::chrono::steady_clock::now();
+      const int q = mail->q;
       serve(team, partial);
       last = r;
       __atomic_store_n(&mail->done, r, __ATOMIC_RELEASE);
+      busy_ns.fetch_add(std::chrono::duration_cast<std::chrono::nanoseconds>(
+                            std::chrono::steady_clock::now() - t0).count(),
+                        std::memory_order_relaxed);
+      experts.fetch_add(q, std::memory_order_relaxed);
       served.fetch_add(1, std::memory_order_relaxed);
     }
   }
@@ -628,6 +636,15 @@ moe_status moe_set_hybrid(moe_cache c, int32_t b_cpu_mbps, int32_t b_pcie_mbps, 
   }
   c->split_bc = b_cpu_mbps;
   c->split_bp = b_pcie_mbps;
+  return MOE_OK;
+}
+
+moe_status moe_hybrid_read(moe_cache c, int64_t* requests, int64_t* experts, double* busy_s) {
+  if (!c) return MOE_E_INVALID;
+  const HybridServer* h = c->hyb;
+  if (requests) *requests = h ? h->served.load() : 0;
+  if (experts) *experts = h ? h->experts.load() : 0;
+  if (busy_s) *busy_s = h ? 1e-9 * (double)h->busy_ns.load() : 0.0;
   return MOE_OK;
 }
 

@@ -27,11 +27,10 @@ void CpuTeam::member(int k) {
   for (;;) {
     const uint64_t g = gen_.load(std::memory_order_acquire);
     if (g == seen) {
-      if (++spins < (1u << 16)) {
+      if (++spins & 1023u)
         _mm_pause();
-      } else {
+      else
         std::this_thread::yield();
-      }
       continue;
     }
     spins = 0;
@@ -47,7 +46,15 @@ void CpuTeam::run(const std::function<void(int)>& job) {
   left_.store(n_ - 1, std::memory_order_release);
   gen_.fetch_add(1, std::memory_order_acq_rel);
   job(0);
-  while (left_.load(std::memory_order_acquire) != 0) _mm_pause();
+  // spin for the members; yield now and then so a member that lost its core (more runnable
+  // threads than cores) gets it back instead of waiting out a scheduler slice
+  unsigned spins = 0;
+  while (left_.load(std::memory_order_acquire) != 0) {
+    if (++spins & 1023u)
+      _mm_pause();
+    else
+      std::this_thread::yield();
+  }
 }
 
 static inline float bf16f(uint16_t b) {

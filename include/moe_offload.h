@@ -225,6 +225,11 @@ moe_status moe_set_prefetch(moe_cache cache, int32_t enable);
 moe_status moe_set_hybrid(moe_cache cache, int32_t b_cpu_mbps, int32_t b_pcie_mbps,
                           int32_t threads);
 
+/* Host-side counters of the hybrid server since moe_set_hybrid started it: requests
+ * answered, CPU experts computed and the seconds spent computing them (zeros when hybrid
+ * decode is off).  Any pointer may be NULL. */
+moe_status moe_hybrid_read(moe_cache cache, int64_t* requests, int64_t* experts, double* busy_s);
+
 /* The CPU expert FFN of the hybrid path, on host buffers (no GPU involved): for t < T,
  * y[t][:] += w[t] * FFN(x[t]) with the bf16 expert blob `blob` (shape's layout), x [T][hidden]
  * bf16, y [T][hidden] fp32, using `threads` host threads.  T in 1..8.  MOE_E_INVALID for a

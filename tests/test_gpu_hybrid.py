@@ -99,3 +99,29 @@ def test_hybrid_rejects_non_bf16():
     with Workbench(wl, groups=0) as wb:
         with pytest.raises(MoeError):
             wb.set_hybrid(*RATES, 4)
+
+
+def test_hybrid_with_resize_at_a_safe_point():
+    """Hybrid decode across an elastic resize (30% -> 12% of the pool at token step 6): CPU
+    misses hold no slot, so the resize keeps the most recently used cached keys exactly as
+    without the split."""
+    from expert_cache_offload_amd.runner import Workbench
+    from oracle.step import Oracle
+    wl = mi.WORKLOADS["qwen35b_decode"].with_layers(2).with_steps(12)
+    new_cap = int(0.12 * wl.n_keys)
+    with Workbench(wl, groups=0) as wb:
+        orc = Oracle(wl, wb.pool, wb.router_np, split=RATES)
+        wb.set_hybrid(*RATES, 6)
+        worst = 0.0
+        for t in range(wl.token_steps):
+            if t == 6:
+                orc.resize(new_cap)
+                wb.resize(new_cap)
+                key_of, stamp, slot_of, n, step, cap = wb.snapshot()
+                assert cap == new_cap and n == orc.cache.n
+                assert list(key_of) == orc.cache.key_of and list(stamp) == orc.cache.stamp
+            for l in range(wl.layers):
+                wb.step(t, l)
+                ref = orc.layer_step(t, l, wb.acts_np[t, l], True)
+                worst = max(worst, compare_step(wb, ref, f"hybrid resize t={t} l={l}") or 0.0)
+    _log(f"hybrid across a resize: max rel-L2 {worst:.2e}")
