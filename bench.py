@@ -160,10 +160,18 @@ def _with_cache_frac(wl, frac: float):
                                fixed_capacity=0)
 
 
+GATE_UP_END = "// ---------------------------------------------------------------- down role"
+
+
 def _ffn_source_hash() -> str:
+    """Hash of the decode FFN source up to the down role: the gate/up kernel and everything it
+    uses (formats, entry resolution); the down and combine kernels that follow do not change
+    the gate/up kernel's traffic."""
     here = os.path.dirname(os.path.abspath(__file__))
     p = os.path.join(here, "expert_cache_offload_amd", "csrc", "ffn_decode.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    text = open(p, "rb").read()
+    cut = text.find(GATE_UP_END.encode())
+    return hashlib.sha256(text[:cut] if cut > 0 else text).hexdigest()[:16]
 
 
 def _traffic_ratio_from_profile(name: str) -> float | None:
@@ -359,8 +367,8 @@ def main() -> None:
 
     import moe_inputs as mi
     from expert_cache_offload_amd import (PROF_ALL, PROF_FILL, PROF_GATE_UP, choose_hybrid,
-                                          moe_cpu_expert_rate, moe_profile_enable,
-                                          moe_profile_read)
+                                          moe_cpu_expert_rate, moe_hybrid_read,
+                                          moe_profile_enable, moe_profile_read)
     from expert_cache_offload_amd.runner import Workbench
 
     wl = mi.WORKLOADS[args.workload]
@@ -432,8 +440,20 @@ def main() -> None:
         if use:
             wb.set_hybrid(int(cpu_rate * 1000), int(pcie * 1000), args.cpu_threads)
             wb.reset()  # from a cold cache again, now splitting misses
+            h0 = moe_hybrid_read(wb.handle)
             warm()
+            # the CPU path's rate re-measured on the warmup's own requests (the probe runs one
+            # expert per call and reads lower): the split uses the rate the server sustained
+            h1 = moe_hybrid_read(wb.handle)
+            busy = h1["busy_s"] - h0["busy_s"]
+            if busy > 0 and h1["experts"] > h0["experts"]:
+                eff = (h1["experts"] - h0["experts"]) * wl.blob_bytes / busy / 1e9
+                hybrid["cpu_rate_warmup_GBps"] = round(eff, 2)
+                wb.set_hybrid(int(eff * 1000), int(pcie * 1000), args.cpu_threads)
+                print(f"[bench] CPU path sustained {eff:.1f} GB/s over the warmup: split "
+                      "recomputed with it", file=sys.stderr, flush=True)
     st0 = wb.stats()
+    hy0 = moe_hybrid_read(wb.handle)
     if not args.no_profile:
         moe_profile_enable(wb.handle, PROF_GATE_UP, args.profile_every)
     # the timed tokens in windows (their rates give median / min / max); a cache resize at a
@@ -463,6 +483,13 @@ def main() -> None:
     wall = sum(dt for _, dt, _ in segments) + (resize_s or 0.0)
     prof = moe_profile_read(wb.handle) if not args.no_profile else None
     st1 = wb.stats()
+    hy1 = moe_hybrid_read(wb.handle)
+    if hybrid is not None and hybrid["mode"] == "hybrid":
+        busy = hy1["busy_s"] - hy0["busy_s"]
+        ex = hy1["experts"] - hy0["experts"]
+        hybrid["cpu_busy_frac"] = round(busy / wall, 4) if wall > 0 else None
+        hybrid["cpu_effective_GBps"] = round(ex * wl.blob_bytes / busy / 1e9, 2) if busy else None
+        hybrid["requests"] = hy1["requests"] - hy0["requests"]
     brk = None
     if not args.no_profile and args.breakdown_steps > 0:
         moe_profile_enable(wb.handle, PROF_ALL)

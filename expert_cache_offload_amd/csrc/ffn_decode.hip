@@ -600,6 +600,7 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
 // has answered this step.  Every partial of a chunk is loaded before any is added (one
 // memory latency per chunk of CH partials).
 constexpr long long kHybridSpin = 1ll << 23;  // ~2 s of polling before giving up (ERR_HYBRID)
+constexpr int kMaxPartials = 640;             // top_k * row splits, checked at launch
 
 __device__ void combine_role(const FfnArgs& a, int cblk) {
   const Dims& d = a.d;
@@ -607,21 +608,24 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
   const int per_tok = (d.H + FT - 1) / FT;
   const int t = cblk / per_tok;
   const int c = (cblk % per_tok) * FT + threadIdx.x;
-  __shared__ int s_pos[32], s_cpu[32];
-  __shared__ int s_ncpu, s_ok;
-  if (threadIdx.x == 0) s_ncpu = v.hdr[HDR_NCPU];
-  __syncthreads();
-  const int ncpu = s_ncpu;
-  if ((int)threadIdx.x < d.K) {
-    const int pos = v.inv_pos[t * d.K + threadIdx.x];
-    s_pos[threadIdx.x] = pos;
-    s_cpu[threadIdx.x] = ncpu > 0 ? v.row_cpu[pos] : 0;
+  const int RS = d.RS, nrouted = d.K * RS;
+  __shared__ int s_row[kMaxPartials];  // yexp row of each routed partial, -1: the CPU's expert
+  __shared__ int s_ok;
+  // one routed partial per thread: the row of the token's j-th expert, split r; the header
+  // word is a vector load so that it goes out with the position loads (a scalar load would
+  // be waited for first)
+  const int ncpu = __hip_atomic_load(&v.hdr[HDR_NCPU], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < nrouted; i += FT) {
+    const int j = i / RS, r = i - j * RS;
+    const int pos = v.inv_pos[t * d.K + j];
+    s_row[i] = ncpu > 0 && v.row_cpu[pos] ? -1 : pos * RS + r;
   }
   if (ncpu > 0 && threadIdx.x == 0) {
     // wait for the host's answer to this step (bounded: an absent server sets ERR_HYBRID)
     const long long step =
         (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
     long long it = 0;
+#pragma nounroll
     while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step &&
            ++it < kHybridSpin)
       __builtin_amdgcn_s_sleep(8);
@@ -631,35 +635,29 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
   __syncthreads();
   if (c >= d.H) return;
   constexpr int CH = 32;
-  const int RS = d.RS, nrouted = d.K * RS, nall = nrouted + (d.has_shared ? RS : 0);
-  float sr = 0.f, ss = 0.f;
-  for (int base = 0; base < nall; base += CH) {
+  float s = 0.f;
+  for (int base = 0; base < nrouted; base += CH) {
+    int row[CH];
     float pv[CH];
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      int i = base + q;
-      i = i < nall ? i : nall - 1;
-      const float* p = i < nrouted
-                           ? v.yexp + ((size_t)s_pos[i / RS] * RS + i % RS) * d.H
-                           : v.yexp_shared + ((size_t)t * RS + (i - nrouted)) * d.H;
-      pv[q] = p[c];
-    }
+    for (int q = 0; q < CH; ++q) row[q] = s_row[base + q < nrouted ? base + q : nrouted - 1];
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-      const int i = base + q;
-      if (i < nrouted) {
-        if (!s_cpu[i / RS]) sr += pv[q];
-      } else if (i < nall) {
-        ss += pv[q];
-      }
-    }
+    for (int q = 0; q < CH; ++q) pv[q] = v.yexp[(size_t)(row[q] < 0 ? 0 : row[q]) * d.H + c];
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+      if (base + q < nrouted && row[q] >= 0) s += pv[q];
   }
-  float s = sr;
   if (ncpu > 0 && s_ok) {
     const float* yc = (const float*)((const unsigned char*)v.mail + mail_y_offset(d.H));
     s += __hip_atomic_load(yc + (size_t)t * d.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s + ss);
+  if (d.has_shared) {
+    float sh[kMaxPartials / 16];
+    const int n = RS < kMaxPartials / 16 ? RS : kMaxPartials / 16;
+    for (int r = 0; r < n; ++r) sh[r] = v.yexp_shared[((size_t)t * RS + r) * d.H + c];
+    for (int r = 0; r < n; ++r) s += sh[r];
+  }
+  a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
 }
 
 template <int FMT>
@@ -765,6 +763,7 @@ hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const v
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
                              int T, int max_entries, int with_combine, int stage,
                              hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (d.K * d.RS > kMaxPartials || d.RS > kMaxPartials / 16) return hipErrorInvalidValue;
   const int nc = with_combine ? T * ((d.H + FT - 1) / FT) : 0;
   FfnArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
             (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
