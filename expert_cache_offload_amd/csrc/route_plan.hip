@@ -39,6 +39,9 @@ struct RouteArgs {
   int split_bc, split_bp;  // hybrid decode: CPU expert rate and PCIe fill rate (MB/s), 0: off
 };
 
+// NTOK: token bound of the step (1, 2, 4 or 8): the router loops are unrolled for it only,
+// which keeps the kernel's code (fetched by every workgroup) small at one token.
+template <int NTOK>
 __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Dims& d = a.d;
@@ -49,23 +52,23 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   // ---------------- phase A: router logits, fp64 accumulation ----------------
   const int waves_total = gridDim.x * (RT / 64);
   for (int e = blockIdx.x * (RT / 64) + wave; e < E; e += waves_total) {
-    double acc[kDecodeMaxTokens];
+    double acc[NTOK];
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = 0.0;
+    for (int t = 0; t < NTOK; ++t) acc[t] = 0.0;
     const uint16_t* wrow = a.wr + (size_t)e * H;
     // chunks of 8 elements per lane, RCH chunks' loads (weights and activations) in flight
     // before any arithmetic
     constexpr int RCH = 4;
     const int nch = (H + 511) / 512;  // H is a multiple of 256: the last chunk may be half
     for (int base = 0; base < nch; base += RCH) {
-      uint4 w[RCH], xv[RCH][kDecodeMaxTokens];
+      uint4 w[RCH], xv[RCH][NTOK];
 #pragma unroll
       for (int k = 0; k < RCH; ++k) {
         const int h = (base + k) * 512 + lane * 8;
         if (base + k < nch && h < H) {
           w[k] = *(const uint4*)(wrow + h);
 #pragma unroll
-          for (int t = 0; t < kDecodeMaxTokens; ++t)
+          for (int t = 0; t < NTOK; ++t)
             if (t < T) xv[k][t] = *(const uint4*)(a.x + (size_t)t * H + h);
         }
       }
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
                                bf16_hi(w[k].y), bf16_lo(w[k].z), bf16_hi(w[k].z),
                                bf16_lo(w[k].w), bf16_hi(w[k].w)};
 #pragma unroll
-          for (int t = 0; t < kDecodeMaxTokens; ++t) {
+          for (int t = 0; t < NTOK; ++t) {
             if (t < T) {
               const uint4 q = xv[k][t];
               const float xf[8] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y),
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) {
+    for (int t = 0; t < NTOK; ++t) {
       if (t < T) {
         double s = acc[t];
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -247,12 +250,18 @@ hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const v
               split_bc, split_bp};
   int grid = (d.E + (RT / 64) - 1) / (RT / 64);
   const size_t lds = route_plan_lds_bytes(d);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)route_plan_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  return launch_timed(route_plan_kernel, dim3(grid), dim3(RT), lds, s, e0, e1, a);
+  auto go = [&](auto kernel) -> hipError_t {
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    return launch_timed(kernel, dim3(grid), dim3(RT), lds, s, e0, e1, a);
+  };
+  if (T <= 1) return go(route_plan_kernel<1>);
+  if (T <= 2) return go(route_plan_kernel<2>);
+  if (T <= 4) return go(route_plan_kernel<4>);
+  return go(route_plan_kernel<kDecodeMaxTokens>);
 }
 
 }  // namespace moe
