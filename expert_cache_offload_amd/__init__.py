@@ -89,6 +89,10 @@ _SIGS = {
     "moe_profile_enable": (_i32, [_vp, _i32, _i32]),
     "moe_set_prefetch": (_i32, [_vp, _i32]),
     "moe_set_hybrid": (_i32, [_vp, _i32, _i32, _i32]),
+    "moe_auto_capacity": (_i32, [ctypes.POINTER(MoeShape), ctypes.c_uint64, ctypes.c_uint64,
+                                 ctypes.c_double, ctypes.POINTER(_i32)]),
+    "moe_pool_write": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
+    "moe_pool_read": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
     "moe_hybrid_read": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                                ctypes.POINTER(ctypes.c_double)]),
     "moe_cpu_expert_ffn": (_i32, [ctypes.POINTER(MoeShape), _vp, _vp, _i32, _vp, _vp, _i32]),
@@ -243,6 +247,25 @@ def moe_set_hybrid(handle: int, b_cpu_mbps: int, b_pcie_mbps: int, threads: int)
     """Split decode misses between fills and in-place CPU compute (b_cpu_mbps 0: off)."""
     _check(_lib.moe_set_hybrid(handle, int(b_cpu_mbps), int(b_pcie_mbps), int(threads)),
            "moe_set_hybrid", handle)
+
+
+def moe_auto_capacity(shape: MoeShape, free_bytes: int, reserve_bytes: int,
+                      offload_ratio: float = -1.0) -> int:
+    """Largest cache capacity that fits the budget (see the header)."""
+    c = _i32(0)
+    _check(_lib.moe_auto_capacity(ctypes.byref(shape), int(free_bytes), int(reserve_bytes),
+                                  float(offload_ratio), ctypes.byref(c)), "moe_auto_capacity")
+    return int(c.value)
+
+
+def moe_pool_write(path: str, shape: MoeShape, pool: int, threads: int = 8) -> None:
+    _check(_lib.moe_pool_write(path.encode(), ctypes.byref(shape), pool, int(threads)),
+           "moe_pool_write")
+
+
+def moe_pool_read(path: str, shape: MoeShape, pool: int, threads: int = 8) -> None:
+    _check(_lib.moe_pool_read(path.encode(), ctypes.byref(shape), pool, int(threads)),
+           "moe_pool_read")
 
 
 def moe_hybrid_read(handle: int) -> dict:

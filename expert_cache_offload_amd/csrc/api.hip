@@ -401,6 +401,40 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_capacity) {
   return make_layout(make_dims(*shape, max_capacity)).total;
 }
 
+moe_status moe_auto_capacity(const moe_shape* shape, uint64_t free_bytes, uint64_t reserve_bytes,
+                             double offload_ratio, int32_t* capacity) {
+  if (!shape_ok(shape) || !capacity) return MOE_E_INVALID;
+  if (offload_ratio >= 1.0) return MOE_E_INVALID;
+  const int64_t n_keys = (int64_t)shape->layers * shape->experts;
+  const int floor_c = shape->max_tokens * shape->top_k < shape->experts
+                          ? shape->max_tokens * shape->top_k
+                          : shape->experts;
+  int64_t top = n_keys < kMaxCapacity ? n_keys : kMaxCapacity;
+  if (offload_ratio >= 0.0) {
+    const int64_t keep = (int64_t)((1.0 - offload_ratio) * (double)n_keys);
+    top = keep < top ? keep : top;
+  }
+  if (free_bytes <= reserve_bytes) return MOE_E_CAPACITY;
+  const uint64_t budget = free_bytes - reserve_bytes;
+  // slots C and the workspace of a handle sized for C must fit the budget; the workspace
+  // grows with C, so the admissible C form a prefix: bisect it
+  auto fits = [&](int64_t c) {
+    const size_t ws = make_layout(make_dims(*shape, (int)c)).total;
+    return (uint64_t)c * (uint64_t)shape->blob_bytes + ws <= budget;
+  };
+  if (top < floor_c || !fits(floor_c)) return MOE_E_CAPACITY;
+  int64_t lo = floor_c, hi = top;  // fits(lo), answer in [lo, hi]
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo + 1) / 2;
+    if (fits(mid))
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  *capacity = (int32_t)lo;
+  return MOE_OK;
+}
+
 moe_status moe_host_pool_alloc(size_t bytes, void** out) {
   if (!out || bytes == 0) return MOE_E_INVALID;
   void* p = nullptr;

@@ -119,6 +119,31 @@ int64_t moe_blob_bytes(int32_t wfmt, int32_t hidden, int32_t inter);
 /* Device workspace bytes for a cache of up to max_capacity slots. */
 size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_capacity);
 
+/* Budget-driven cache size ("FreeToken vs vLLM on one RTX 3090", Runtime configurations: an
+ * automatic cache; "FreeToken: az VRAM ile büyük MoE modelleri", "KV cache": a KV floor is
+ * reserved first; "FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理": --offload-ratio r keeps the
+ * fraction 1 - r of the experts on the GPU).  *capacity = the largest C with
+ * C * blob_bytes + moe_workspace_bytes(shape, C) <= free_bytes - reserve_bytes (reserve: the
+ * KV floor and anything else that must stay resident), at most layers * experts, at most the
+ * slot limit of a handle (4,096), and at most floor((1 - offload_ratio) * layers * experts)
+ * when 0 <= offload_ratio < 1 (a negative ratio: no such limit).  Host arithmetic only.
+ * MOE_E_CAPACITY when not even the floor min(max_tokens * top_k, experts) fits;
+ * MOE_E_INVALID for a bad shape or offload_ratio >= 1. */
+moe_status moe_auto_capacity(const moe_shape* shape, uint64_t free_bytes, uint64_t reserve_bytes,
+                             double offload_ratio, int32_t* capacity);
+
+/* Expert pool files in the runtime layout (the FreeToken paper summary, execution-layer
+ * paragraph: weights merged ahead of time into the runtime layout load straight into their
+ * final place).  A 64-byte header (magic "MOEPOOL1", int32 layers, experts, hidden, inter,
+ * wfmt, pad, int64 blob_bytes, int64 blob count) and then the layers * experts blobs in key
+ * order.  moe_pool_write stores a pool; moe_pool_read fills `pool` (host memory of
+ * layers * experts * blob_bytes bytes, normally from moe_host_pool_alloc, so the blobs land
+ * in pinned memory directly) with `threads` parallel readers.  MOE_E_INVALID on an I/O error,
+ * a header that does not match `shape`, or a file of the wrong size. */
+moe_status moe_pool_write(const char* path, const moe_shape* shape, const void* pool,
+                          int32_t threads);
+moe_status moe_pool_read(const char* path, const moe_shape* shape, void* pool, int32_t threads);
+
 /* Pinned, device-accessible host memory for the expert pool (hipHostMalloc).
  * Returns MOE_E_NOMEM when the allocation fails.  Free with moe_host_pool_free. */
 moe_status moe_host_pool_alloc(size_t bytes, void** out);
