@@ -269,6 +269,17 @@ def run_prefill(args, wl) -> None:
     st = wb.stats()
     db_prefetch = chunk(ab_groups)
     no_prefetch = chunk(ab_groups, prefetch=False)
+    # the matrix-core kernels without concurrent fills: a chunk in stream order (each layer's
+    # fills, then its FFN), gate/up and down timed
+    wb.groups = 0
+    wb.prefetch = False
+    wb.reset()
+    moe_profile_enable(wb.handle, PROF_GATE_UP | PROF_DOWN)
+    for l in range(L):
+        wb.step(0, l)
+    torch.cuda.synchronize()
+    iso = moe_profile_read(wb.handle)
+    moe_profile_enable(wb.handle, 0)
     fl_gu = 2.0 * T * K * (2 * I) * H * L  # gate/up FLOPs of the chunk (every routed row)
     fl_dn = 2.0 * T * K * I * H * L
     gu_s = prof["gate_up"]["ms"] / 1e3
@@ -307,6 +318,15 @@ def run_prefill(args, wl) -> None:
                                             max(1, prof["gate_up"]["launches"]), 1),
                      "algorithmic_flops_per_chunk": fl_gu},
         "down_kernel_TFLOPs": round(fl_dn / dn_s / 1e12, 1) if dn_s > 0 else None,
+        "isolated": {"note": "one chunk with each layer's fills before its FFN (no concurrent "
+                             "fill traffic): the GEMMs' own rate",
+                     "gate_up_TFLOPs": round(fl_gu / (iso["gate_up"]["ms"] / 1e3) / 1e12, 1)
+                     if iso["gate_up"]["ms"] else None,
+                     "gate_up_frac": round(fl_gu / (iso["gate_up"]["ms"] / 1e3) / 1e12 /
+                                           MFMA_BF16_PEAK_TFLOPS, 4)
+                     if iso["gate_up"]["ms"] else None,
+                     "down_TFLOPs": round(fl_dn / (iso["down"]["ms"] / 1e3) / 1e12, 1)
+                     if iso["down"]["ms"] else None},
         "cpu_baseline": cpu,
         "fill": {"bytes_per_chunk": fill_bytes, "misses_per_chunk": misses,
                  "kernel_GBps": round(fill_bytes / fk_s / 1e9, 2) if fk_s > 0 else None,

@@ -202,38 +202,38 @@ __device__ __forceinline__ float dot2(bf16x2v w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2v, x), acc, false);
 }
 
-// sum over one 16-byte weight chunk (EPL weights, unscaled codes) times EPL activations
-// given as EPL/2 words of bf16 pairs; acc is added
+// One 16-byte weight chunk widened to EPL/2 words of bf16 pairs (fp8 and e2m1 codes are
+// exact in bf16; unscaled), once per chunk whatever the number of tokens.
 template <int FMT>
-__device__ __forceinline__ float chunk_dot(const u32x4v& w, const uint32_t* xw, float acc);
+__device__ __forceinline__ void widen(const u32x4v& w, uint32_t* o);
 template <>
-__device__ __forceinline__ float chunk_dot<FMT_BF16>(const u32x4v& w, const uint32_t* xw,
-                                                     float acc) {
-  acc = dot2(w.x, xw[0], acc);
-  acc = dot2(w.y, xw[1], acc);
-  acc = dot2(w.z, xw[2], acc);
-  return dot2(w.w, xw[3], acc);
+__device__ __forceinline__ void widen<FMT_BF16>(const u32x4v& w, uint32_t* o) {
+  o[0] = w.x; o[1] = w.y; o[2] = w.z; o[3] = w.w;
 }
 template <>
-__device__ __forceinline__ float chunk_dot<FMT_FP8>(const u32x4v& w, const uint32_t* xw,
-                                                    float acc) {
+__device__ __forceinline__ void widen<FMT_FP8>(const u32x4v& w, uint32_t* o) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, false), xw[2 * q], acc);
-    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, true), xw[2 * q + 1], acc);
+    o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, false));
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, true));
   }
-  return acc;
 }
 template <>
-__device__ __forceinline__ float chunk_dot<FMT_MXFP4>(const u32x4v& w, const uint32_t* xw,
-                                                      float acc) {
+__device__ __forceinline__ void widen<FMT_MXFP4>(const u32x4v& w, uint32_t* o) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 0), xw[4 * q], acc);
-    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 1), xw[4 * q + 1], acc);
-    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 2), xw[4 * q + 2], acc);
-    acc = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 3), xw[4 * q + 3], acc);
+    o[4 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 0));
+    o[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 1));
+    o[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 2));
+    o[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 3));
   }
+}
+
+// acc + sum over N words of bf16 pairs: weights (widened) times activations
+template <int N>
+__device__ __forceinline__ float wdot(const uint32_t* ww, const uint32_t* xw, float acc) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) acc = dot2(ww[j], xw[j], acc);
   return acc;
 }
 
@@ -387,6 +387,12 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
     for (int k = 0; k < GN; ++k) {
       const int c = (kb + k) * 64 + lane;
       if (c < ngq) {
+        constexpr int NW = EPL / 2;
+        uint32_t ag0[NW], au0[NW], ag1[NW], au1[NW];
+        widen<FMT>(wg0[k], ag0);
+        widen<FMT>(wu0[k], au0);
+        widen<FMT>(wg1[k], ag1);
+        widen<FMT>(wu1[k], au1);
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
           if (t < ntok) {
@@ -407,15 +413,15 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
               }
             }
             if constexpr (F::SB > 0) {
-              g0[t] += sg0[k] * chunk_dot<FMT>(wg0[k], xw, 0.f);
-              u0[t] += su0[k] * chunk_dot<FMT>(wu0[k], xw, 0.f);
-              g1[t] += sg1[k] * chunk_dot<FMT>(wg1[k], xw, 0.f);
-              u1[t] += su1[k] * chunk_dot<FMT>(wu1[k], xw, 0.f);
+              g0[t] += sg0[k] * wdot<NW>(ag0, xw, 0.f);
+              u0[t] += su0[k] * wdot<NW>(au0, xw, 0.f);
+              g1[t] += sg1[k] * wdot<NW>(ag1, xw, 0.f);
+              u1[t] += su1[k] * wdot<NW>(au1, xw, 0.f);
             } else {
-              g0[t] = chunk_dot<FMT>(wg0[k], xw, g0[t]);
-              u0[t] = chunk_dot<FMT>(wu0[k], xw, u0[t]);
-              g1[t] = chunk_dot<FMT>(wg1[k], xw, g1[t]);
-              u1[t] = chunk_dot<FMT>(wu1[k], xw, u1[t]);
+              g0[t] = wdot<NW>(ag0, xw, g0[t]);
+              u0[t] = wdot<NW>(au0, xw, u0[t]);
+              g1[t] = wdot<NW>(ag1, xw, g1[t]);
+              u1[t] = wdot<NW>(au1, xw, u1[t]);
             }
           }
         }
@@ -652,10 +658,15 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
     s += __hip_atomic_load(yc + (size_t)t * d.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if (d.has_shared) {
-    float sh[kMaxPartials / 16];
-    const int n = RS < kMaxPartials / 16 ? RS : kMaxPartials / 16;
-    for (int r = 0; r < n; ++r) sh[r] = v.yexp_shared[((size_t)t * RS + r) * d.H + c];
-    for (int r = 0; r < n; ++r) s += sh[r];
+    for (int r0 = 0; r0 < RS; r0 += 8) {  // the shared expert's row splits, 8 loads at a time
+      float sh[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        sh[q] = v.yexp_shared[((size_t)t * RS + (r0 + q < RS ? r0 + q : RS - 1)) * d.H + c];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (r0 + q < RS) s += sh[q];
+    }
   }
   a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
 }
@@ -763,7 +774,7 @@ hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const v
                              const void* shared_blob, void* y, int sel, int group, int ngroups,
                              int T, int max_entries, int with_combine, int stage,
                              hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (d.K * d.RS > kMaxPartials || d.RS > kMaxPartials / 16) return hipErrorInvalidValue;
+  if (d.K * d.RS > kMaxPartials) return hipErrorInvalidValue;
   const int nc = with_combine ? T * ((d.H + FT - 1) / FT) : 0;
   FfnArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
             (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
