@@ -98,7 +98,9 @@ __device__ inline unsigned char* plan_carve(const Dims& d, unsigned char* p, Pla
   s.aslot = (int*)p;      p += sizeof(int) * umax;
   s.avkey = (int*)p;      p += sizeof(int) * umax;
   s.hitl = (int*)p;       p += sizeof(int) * umax;
-  return (unsigned char*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
+  // align by adding an offset: a round trip through an integer would lose the pointer's
+  // LDS address space, and every access through it would become a flat access
+  return p + ((16 - ((uintptr_t)p & 15)) & 15);
 }
 
 // Static shared scratch of the plan.

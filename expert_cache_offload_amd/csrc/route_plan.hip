@@ -149,7 +149,8 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     const double z = s_z[i];
     const double* zt = s_z + (size_t)t * E;
     int rank = 0;
-    for (int e2 = 0; e2 < E; ++e2) {
+#pragma unroll 8
+    for (int e2 = 0; e2 < E; ++e2) {  // 8 LDS reads in flight per step (E % 8 need not be 0)
       const double z2 = zt[e2];
       rank += (z2 > z) || (z2 == z && e2 < e);
     }
