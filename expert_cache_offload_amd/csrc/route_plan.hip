@@ -143,20 +143,31 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   __syncthreads();
 
   // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
-  // the experts of rank < K are the selection, in order.
-  for (int i = threadIdx.x; i < T * E; i += RT) {
-    const int t = i / E, e = i - t * E;
-    const double z = s_z[i];
-    const double* zt = s_z + (size_t)t * E;
-    int rank = 0;
+  // the experts of rank < K are the selection, in order.  P adjacent lanes count one
+  // (token, expert) pair, each over 1/P of the experts, and add their counts (P = 2 measured
+  // best at E = 128: one pair per thread of the workgroup at one token).
+  {
+    constexpr int P = 2;
+    const int part = (E + P - 1) / P;
+    for (int idx = threadIdx.x; idx < P * T * E; idx += RT) {
+      const int i = idx / P, h = idx % P;
+      const int t = i / E, e = i - t * E;
+      const double z = s_z[i];
+      const double* zt = s_z + (size_t)t * E;
+      const int e_beg = h * part, e_end = e_beg + part < E ? e_beg + part : E;
+      int rank = 0;
 #pragma unroll 8
-    for (int e2 = 0; e2 < E; ++e2) {  // 8 LDS reads in flight per step (E % 8 need not be 0)
-      const double z2 = zt[e2];
-      rank += (z2 > z) || (z2 == z && e2 < e);
-    }
-    if (rank < K) {
-      s_tk_idx[t * K + rank] = e;
-      s_tk_z[t * K + rank] = z;
+      for (int e2 = e_beg; e2 < e_end; ++e2) {  // 8 LDS reads in flight per step
+        const double z2 = zt[e2];
+        rank += (z2 > z) || (z2 == z && e2 < e);
+      }
+#pragma unroll
+      for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);  // the P lanes are adjacent
+                                                                     // and all active
+      if (h == 0 && rank < K) {
+        s_tk_idx[t * K + rank] = e;
+        s_tk_z[t * K + rank] = z;
+      }
     }
   }
   __syncthreads();
