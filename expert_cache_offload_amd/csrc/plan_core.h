@@ -130,21 +130,22 @@ __host__ __device__ inline int miss_split(int m, int bc, int bp) {
 }
 
 // Cache state the plan reads, loaded once at its start.
+constexpr int kRowsPerThread = 1024 / RT;  // slot_of row entries per thread (E <= 1024)
 struct PlanState {
   int n, C;
   long long step;
   uint32_t st[kSlotsPerThread], key[kSlotsPerThread];  // this thread's occupied slots
+  int srow[kRowsPerThread];                            // this thread's slot_of row entries
 };
 
-// All threads: reset the per-expert arrays, read this layer's slot_of row and the control
-// words, then the occupied slots' (stamp, key) into registers.  The caller syncs before
-// reading the LDS arrays.
-__device__ inline void plan_begin(const Dims& d, const Dev& v, int layer, PlanLds& s,
-                                  PlanState& ps) {
-  for (int e = threadIdx.x; e < d.E; e += RT) {
-    s.cnt[e] = 0;
-    s.uidx[e] = -1;
-    s.srow[e] = v.slot_of[layer * d.E + e];
+// All threads: issue every load of the plan's start - this layer's slot_of row, the control
+// words and the (stamp, key) of every slot the handle can hold (unconditionally: a bound on
+// the occupancy would make these loads wait for the control words) - into registers.
+__device__ inline void plan_begin_load(const Dims& d, const Dev& v, int layer, PlanState& ps) {
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int e = (int)threadIdx.x + j * RT;
+    ps.srow[j] = e < d.E ? v.slot_of[layer * d.E + e] : -1;
   }
   ps.n = v.ctrl[CTRL_N];
   ps.C = v.ctrl[CTRL_C];
@@ -152,13 +153,39 @@ __device__ inline void plan_begin(const Dims& d, const Dev& v, int layer, PlanLd
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int i = (int)threadIdx.x + j * RT;
-    ps.st[j] = 0xffffffffu;
-    ps.key[j] = 0xffffffffu;
-    if (i < ps.n) {
-      ps.st[j] = (uint32_t)v.stamp[i];
-      ps.key[j] = (uint32_t)v.key_of[i];
+    const bool in = i < d.max_capacity;
+    ps.st[j] = in ? (uint32_t)v.stamp[i] : 0xffffffffu;
+    ps.key[j] = in ? (uint32_t)v.key_of[i] : 0xffffffffu;
+  }
+}
+
+// All threads, after plan_begin_load: the per-expert LDS arrays, and the slots beyond the
+// occupancy marked empty.  The caller syncs before reading the LDS arrays.
+__device__ inline void plan_begin_store(const Dims& d, PlanLds& s, PlanState& ps) {
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int e = (int)threadIdx.x + j * RT;
+    if (e < d.E) {
+      s.cnt[e] = 0;
+      s.uidx[e] = -1;
+      s.srow[e] = ps.srow[j];
     }
   }
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int i = (int)threadIdx.x + j * RT;
+    if (i >= ps.n) {
+      ps.st[j] = 0xffffffffu;
+      ps.key[j] = 0xffffffffu;
+    }
+  }
+}
+
+// Both parts at once (plans whose start has no other loads to overlap).
+__device__ inline void plan_begin(const Dims& d, const Dev& v, int layer, PlanLds& s,
+                                  PlanState& ps) {
+  plan_begin_load(d, v, layer, ps);
+  plan_begin_store(d, s, ps);
 }
 
 // After s.cnt holds the step's assignments per expert (synced): U ascending (ballot /

@@ -133,13 +133,17 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   __shared__ PlanTmp pt;
   PlanState ps;
 
-  // Every global read of the plan goes out together: the logits, this layer's row of
-  // slot_of, the control words and the occupied slots' (stamp, key).
-  for (int i = threadIdx.x; i < T * E; i += RT) {
+  // Every global read of the plan goes out together: the logits (the first RT of them into
+  // registers), this layer's row of slot_of, the control words and the slots' (stamp, key);
+  // the LDS stores follow.
+  const double z0 = (int)threadIdx.x < T * E ? v.logits[threadIdx.x] : 0.0;
+  plan_begin_load(d, v, layer, ps);
+  if ((int)threadIdx.x < T * E) s_z[threadIdx.x] = (z0 == z0) ? z0 : -__builtin_huge_val();
+  for (int i = threadIdx.x + RT; i < T * E; i += RT) {
     const double z = v.logits[i];
     s_z[i] = (z == z) ? z : -__builtin_huge_val();  // NaN ranks as -inf
   }
-  plan_begin(d, v, layer, s, ps);
+  plan_begin_store(d, s, ps);
   __syncthreads();
 
   // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
