@@ -93,6 +93,8 @@ _SIGS = {
                                  ctypes.c_double, ctypes.POINTER(_i32)]),
     "moe_pool_write": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
     "moe_pool_read": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
+    "moe_set_hybrid_timeout": (_i32, [_vp, _i64]),
+    "moe_hybrid_hold": (_i32, [_vp, _i32]),
     "moe_hybrid_read": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                                ctypes.POINTER(ctypes.c_double)]),
     "moe_cpu_expert_ffn": (_i32, [ctypes.POINTER(MoeShape), _vp, _vp, _i32, _vp, _vp, _i32]),
@@ -266,6 +268,15 @@ def moe_pool_write(path: str, shape: MoeShape, pool: int, threads: int = 8) -> N
 def moe_pool_read(path: str, shape: MoeShape, pool: int, threads: int = 8) -> None:
     _check(_lib.moe_pool_read(path.encode(), ctypes.byref(shape), pool, int(threads)),
            "moe_pool_read")
+
+
+def moe_set_hybrid_timeout(handle: int, microseconds: int) -> None:
+    _check(_lib.moe_set_hybrid_timeout(handle, int(microseconds)), "moe_set_hybrid_timeout",
+           handle)
+
+
+def moe_hybrid_hold(handle: int, hold: bool) -> None:
+    _check(_lib.moe_hybrid_hold(handle, int(bool(hold))), "moe_hybrid_hold", handle)
 
 
 def moe_hybrid_read(handle: int) -> dict:

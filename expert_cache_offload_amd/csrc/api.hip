@@ -189,6 +189,7 @@ Dev make_dev(void* ws, const Layout& L) {
   v.row_cpu = (int*)(b + L.row_cpu);
   v.cpu_key = (int*)(b + L.cpu_key);
   v.mail = nullptr;
+  v.hyb_timeout_ticks = 200000000;  // 2 s
   return v;
 }
 
@@ -298,6 +299,7 @@ struct HybridServer {
   int threads = 1;
   std::thread th;
   std::atomic<bool> stop{false};
+  std::atomic<bool> hold{false};      // leave requests unanswered (failure-path tests)
   std::atomic<long long> served{0};   // requests answered
   std::atomic<long long> experts{0};  // CPU experts computed
   std::atomic<long long> busy_ns{0};  // time spent computing them
@@ -321,15 +323,20 @@ struct HybridServer {
     CpuTeam team(threads);
     std::vector<float> partial((size_t)threads * kDecodeMaxTokens * d.H);
     unsigned spins = 0;
+    auto idle_since = std::chrono::steady_clock::now();
     while (!stop.load(std::memory_order_acquire)) {
       const long long r = __atomic_load_n(&mail->req, __ATOMIC_ACQUIRE);
-      if (r == last) {
+      if (r == last || hold.load(std::memory_order_acquire)) {
+        // poll hot while steps arrive; after 50 ms without one, every 50 us
         if (++spins < 4096) {
           _mm_pause();
-        } else {
-          spins = 0;
-          std::this_thread::yield();
+          continue;
         }
+        spins = 0;
+        if (std::chrono::steady_clock::now() - idle_since > std::chrono::milliseconds(50))
+          std::this_thread::sleep_for(std::chrono::microseconds(50));
+        else
+          std::this_thread::yield();
         continue;
       }
       const auto t0 = std::chrono::steady_clock::now();
@@ -342,6 +349,7 @@ struct HybridServer {
                         std::memory_order_relaxed);
       experts.fetch_add(q, std::memory_order_relaxed);
       served.fetch_add(1, std::memory_order_relaxed);
+      idle_since = std::chrono::steady_clock::now();
     }
   }
 };
@@ -670,6 +678,19 @@ moe_status moe_set_hybrid(moe_cache c, int32_t b_cpu_mbps, int32_t b_pcie_mbps, 
   }
   c->split_bc = b_cpu_mbps;
   c->split_bp = b_pcie_mbps;
+  return MOE_OK;
+}
+
+moe_status moe_set_hybrid_timeout(moe_cache c, int64_t microseconds) {
+  if (!c || microseconds < 1) return MOE_E_INVALID;
+  if (c->state != State::Idle) return MOE_E_BUSY;
+  c->v.hyb_timeout_ticks = microseconds * 100;  // the GPU's constant clock runs at 100 MHz
+  return MOE_OK;
+}
+
+moe_status moe_hybrid_hold(moe_cache c, int32_t hold) {
+  if (!c || !c->hyb || (hold != 0 && hold != 1)) return MOE_E_INVALID;
+  c->hyb->hold.store(hold != 0, std::memory_order_release);
   return MOE_OK;
 }
 

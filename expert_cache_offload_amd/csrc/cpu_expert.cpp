@@ -6,6 +6,7 @@
 
 #include <immintrin.h>
 
+#include <chrono>
 #include <cmath>
 #include <cstring>
 
@@ -24,15 +25,21 @@ CpuTeam::~CpuTeam() {
 void CpuTeam::member(int k) {
   uint64_t seen = 0;
   unsigned spins = 0;
+  auto idle_since = std::chrono::steady_clock::now();
   for (;;) {
     const uint64_t g = gen_.load(std::memory_order_acquire);
     if (g == seen) {
-      if (++spins & 1023u)
+      // spin while jobs arrive; yield now and then; after 50 ms without a job, nap 50 us
+      if (++spins & 1023u) {
         _mm_pause();
-      else
+      } else if (std::chrono::steady_clock::now() - idle_since > std::chrono::milliseconds(50)) {
+        std::this_thread::sleep_for(std::chrono::microseconds(50));
+      } else {
         std::this_thread::yield();
+      }
       continue;
     }
+    idle_since = std::chrono::steady_clock::now();
     spins = 0;
     seen = g;
     if (stop_.load(std::memory_order_acquire)) return;

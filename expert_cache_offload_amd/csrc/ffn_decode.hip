@@ -605,7 +605,6 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
 // decode), and y_cpu[t] (their weighted sum, from the host mailbox) is added once the host
 // has answered this step.  Every partial of a chunk is loaded before any is added (one
 // memory latency per chunk of CH partials).
-constexpr long long kHybridSpin = 1ll << 23;  // ~2 s of polling before giving up (ERR_HYBRID)
 constexpr int kMaxPartials = 640;             // top_k * row splits, checked at launch
 
 __device__ void combine_role(const FfnArgs& a, int cblk) {
@@ -627,16 +626,22 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
     s_row[i] = ncpu > 0 && v.row_cpu[pos] ? -1 : pos * RS + r;
   }
   if (ncpu > 0 && threadIdx.x == 0) {
-    // wait for the host's answer to this step (bounded: an absent server sets ERR_HYBRID)
+    // wait for the host's answer to this step, bounded by the handle's timeout on the GPU's
+    // constant 100 MHz clock (no answer in time: ERR_HYBRID, and the step goes on without it)
     const long long step =
         (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
-    long long it = 0;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = true;
 #pragma nounroll
-    while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step &&
-           ++it < kHybridSpin)
+    while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)v.hyb_timeout_ticks) {
+        ok = false;
+        break;
+      }
       __builtin_amdgcn_s_sleep(8);
-    s_ok = it < kHybridSpin;
-    if (!s_ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
+    }
+    s_ok = ok;
+    if (!ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
   }
   __syncthreads();
   if (c >= d.H) return;

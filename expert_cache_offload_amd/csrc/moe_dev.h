@@ -153,6 +153,7 @@ struct Dev {
   int* row_cpu;        // [adec] 1: the row's expert is computed by the CPU (hybrid decode)
   int* cpu_key;        // [umax] keys of the step's CPU misses, ascending expert
   HybMail* mail;       // device view of the hybrid mailbox, or null
+  long long hyb_timeout_ticks;  // longest wait for the host's answer, 100 MHz clock ticks
 };
 
 // Where a plan writes its outputs: the step plan or a prefetch plan.

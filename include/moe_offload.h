@@ -241,14 +241,24 @@ moe_status moe_set_prefetch(moe_cache cache, int32_t enable);
  * no slot, evict nothing and are not stamped.  The route kernel posts them to a pinned
  * mailbox that a server thread of this handle polls; `threads` host threads (the server
  * and its team, which spin while idle) compute them from the host pool, and the combine
- * kernel adds their sum once the host has answered (after ~2 s without an answer it gives
- * up and the next moe_stats / moe_cache_snapshot returns MOE_E_HYBRID).  b_cpu_mbps = 0
+ * kernel adds their sum once the host has answered (after 2 s without an answer - see
+ * moe_set_hybrid_timeout - it gives up and the next moe_stats / moe_cache_snapshot returns
+ * MOE_E_HYBRID).  b_cpu_mbps = 0
  * turns the split off (and stops the threads).  bf16 weights only (MOE_E_INVALID
  * otherwise); MOE_E_BUSY while a step is in flight; MOE_E_NOMEM if the mailbox cannot be
  * pinned.  Choosing the mode is the caller's: the pages switch to the split only when the
  * CPU expert rate is at least 2.0x the offload rate. */
 moe_status moe_set_hybrid(moe_cache cache, int32_t b_cpu_mbps, int32_t b_pcie_mbps,
                           int32_t threads);
+
+/* Longest time the combine kernel waits for the host's answer to a hybrid step before it
+ * gives up (ERR_HYBRID: moe_stats / moe_cache_snapshot then return MOE_E_HYBRID), measured on
+ * the GPU's constant clock; default 2 s.  MOE_E_BUSY while a step is in flight. */
+moe_status moe_set_hybrid_timeout(moe_cache cache, int64_t microseconds);
+
+/* Failure-path testing: hold = 1 makes the hybrid server leave requests unanswered (the
+ * combine then times out as above); hold = 0 resumes.  MOE_E_INVALID without hybrid decode. */
+moe_status moe_hybrid_hold(moe_cache cache, int32_t hold);
 
 /* Host-side counters of the hybrid server since moe_set_hybrid started it: requests
  * answered, CPU experts computed and the seconds spent computing them (zeros when hybrid

@@ -125,3 +125,30 @@ def test_hybrid_with_resize_at_a_safe_point():
                 ref = orc.layer_step(t, l, wb.acts_np[t, l], True)
                 worst = max(worst, compare_step(wb, ref, f"hybrid resize t={t} l={l}") or 0.0)
     _log(f"hybrid across a resize: max rel-L2 {worst:.2e}")
+
+
+def test_hybrid_host_silence_is_bounded_and_reported():
+    """Failure path, forced from the host: the server holds its answers, the combine gives up
+    after the handle's (here 2 ms) timeout, the steps complete, and the next counter read
+    reports MOE_E_HYBRID."""
+    import time
+
+    from expert_cache_offload_amd import (MOE_E_HYBRID, MoeError, moe_hybrid_hold,
+                                          moe_set_hybrid_timeout)
+    from expert_cache_offload_amd.runner import Workbench
+    wl = mi.WORKLOADS["tiny"].with_steps(4)
+    with Workbench(wl, groups=0) as wb:
+        wb.set_hybrid(*RATES, 2)
+        moe_set_hybrid_timeout(wb.handle, 2000)
+        moe_hybrid_hold(wb.handle, True)
+        t0 = time.perf_counter()
+        for t in range(3):
+            wb.step(t, 0)
+        wb.sync()
+        dt = time.perf_counter() - t0
+        with pytest.raises(MoeError) as ei:
+            wb.stats()
+        assert ei.value.status == MOE_E_HYBRID
+        moe_hybrid_hold(wb.handle, False)
+    _log(f"host silence: 3 steps in {dt * 1e3:.1f} ms with a 2 ms bound each")
+    assert dt < 2.0
