@@ -93,6 +93,7 @@ _SIGS = {
                                  ctypes.c_double, ctypes.POINTER(_i32)]),
     "moe_pool_write": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
     "moe_pool_read": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
+    "moe_miss_split": (_i32, [_i32, _i32, _i32]),
     "moe_set_hybrid_timeout": (_i32, [_vp, _i64]),
     "moe_hybrid_hold": (_i32, [_vp, _i32]),
     "moe_hybrid_read": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
@@ -268,6 +269,10 @@ def moe_pool_write(path: str, shape: MoeShape, pool: int, threads: int = 8) -> N
 def moe_pool_read(path: str, shape: MoeShape, pool: int, threads: int = 8) -> None:
     _check(_lib.moe_pool_read(path.encode(), ctypes.byref(shape), pool, int(threads)),
            "moe_pool_read")
+
+
+def moe_miss_split(misses: int, b_cpu_mbps: int, b_pcie_mbps: int) -> int:
+    return int(_lib.moe_miss_split(int(misses), int(b_cpu_mbps), int(b_pcie_mbps)))
 
 
 def moe_set_hybrid_timeout(handle: int, microseconds: int) -> None:

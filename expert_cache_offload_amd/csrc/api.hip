@@ -14,6 +14,7 @@
 #include "../../include/moe_offload.h"
 #include "cpu_expert.h"
 #include "moe_dev.h"
+#include "plan_core.h"
 
 namespace moe {
 hipError_t launch_route_plan(const Dims& d, const Dev& v, const void* x, const void* wr,
@@ -679,6 +680,11 @@ moe_status moe_set_hybrid(moe_cache c, int32_t b_cpu_mbps, int32_t b_pcie_mbps, 
   c->split_bc = b_cpu_mbps;
   c->split_bp = b_pcie_mbps;
   return MOE_OK;
+}
+
+int32_t moe_miss_split(int32_t misses, int32_t b_cpu_mbps, int32_t b_pcie_mbps) {
+  if (misses < 0 || b_cpu_mbps < 0 || b_pcie_mbps < 0) return -1;
+  return miss_split(misses, b_cpu_mbps, b_pcie_mbps);
 }
 
 moe_status moe_set_hybrid_timeout(moe_cache c, int64_t microseconds) {

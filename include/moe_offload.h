@@ -251,6 +251,10 @@ moe_status moe_set_prefetch(moe_cache cache, int32_t enable);
 moe_status moe_set_hybrid(moe_cache cache, int32_t b_cpu_mbps, int32_t b_pcie_mbps,
                           int32_t threads);
 
+/* The split the route kernel applies (same code): CPU misses of `misses`, or -1 for a
+ * negative argument.  Host arithmetic, for checking the closed form. */
+int32_t moe_miss_split(int32_t misses, int32_t b_cpu_mbps, int32_t b_pcie_mbps);
+
 /* Longest time the combine kernel waits for the host's answer to a hybrid step before it
  * gives up (ERR_HYBRID: moe_stats / moe_cache_snapshot then return MOE_E_HYBRID), measured on
  * the GPU's constant clock; default 2 s.  MOE_E_BUSY while a step is in flight. */

@@ -65,3 +65,19 @@ def test_mode_choice_threshold():
     assert not ecoa.choose_hybrid(52.4, 51.5)   # the pages' bf16 probe: 1.02x -> offload
     assert ecoa.choose_hybrid(124.5, 56.0)
     assert not ecoa.choose_hybrid(0.0, 51.3)    # no CPU path
+
+
+def test_kernel_closed_form_split_equals_oracle_minimiser():
+    """The route kernel's closed form (floor of the equal-finish point or the next integer),
+    called on the host, against the oracle's exhaustive makespan minimiser."""
+    from oracle.split import miss_split
+    rng = np.random.default_rng(9)
+    cases = [(m, bc, bp) for m in range(0, 130) for bc, bp in
+             ((0, 56_000), (56_000, 0), (50_000, 50_000), (124_500, 56_000), (7, 3), (1, 10**6))]
+    cases += [(int(rng.integers(0, 129)), int(rng.integers(0, 400_000)),
+               int(rng.integers(0, 400_000))) for _ in range(3000)]
+    for m, bc, bp in cases:
+        if bc == 0 and bp == 0:
+            continue
+        assert ecoa.moe_miss_split(m, bc, bp) == miss_split(m, bc, bp), (m, bc, bp)
+    assert ecoa.moe_miss_split(-1, 1, 1) == -1
