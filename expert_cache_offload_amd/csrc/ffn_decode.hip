@@ -12,22 +12,25 @@
 // is read once, in coalesced 16-byte lanes, with many loads in flight per wave.  Per group
 // of experts two streaming kernels run back to back, and the step ends with a combine:
 //   gate/up  - a workgroup owns 8 intermediate rows of one expert; each wave streams two
-//              gate|up rows (contiguous 2H elements each) with both rows' loads in flight,
-//              reduces across the wave, and writes a = silu(g) * u * w_token (fp32) for
-//              every token routed to the expert;
-//   down     - a workgroup owns a 128-byte-wide column block of the stored transpose WdT
-//              (64 bytes for MXFP4) and half or all of its rows; each thread streams a
-//              contiguous run of rows for 16 (8) bytes of columns, so no partial sums over
-//              the intermediate dimension leave the workgroup; it writes the expert's
-//              output columns (fp32);
-//   combine  - y[t] = bf16(sum over the token's k experts (+ shared) in a fixed order).
-// Kernel boundaries carry the dependencies: on gfx950 an agent-scope fence is an L2
-// write-back plus invalidate, far too costly per workgroup while fills stream into HBM.
+//              gate|up rows (contiguous 2H elements each) with every weight load in flight
+//              before any is used, reduces across the wave, and writes
+//              a = silu(g) * u * w_token (fp32) for every token routed to the expert;
+//   down     - a workgroup owns a 128-column block of the stored transpose WdT (256 columns
+//              for fp8 / MXFP4) and 1/RS of its rows; each thread streams a contiguous run of
+//              rows for 16 (8) bytes of columns, so no partial sums over the intermediate
+//              dimension leave the workgroup except one per row split; it writes the
+//              expert's output columns (fp32);
+//   combine  - y[t] = bf16(sum over the token's k experts' row splits, + the CPU experts'
+//              sum in hybrid decode, + the shared expert) in a fixed order.
+// Kernel boundaries carry the dependencies: on gfx950 an agent-scope release / acquire per
+// workgroup is an L2 write-back / invalidate, far costlier than a second launch.
 // The route kernel publishes a packed entry table (slot, token count, first row, miss
 // index) so a workgroup reaches its weights after two dependent loads.
 // Every expert is read once per step whatever number of tokens use it (cross-request
-// sharing at batch > 1).  fp8 e4m3fn and e2m1 are decoded with gfx950's packed conversions;
-// block scales are applied once per block of rows (down) or per 16-byte chunk (gate/up).
+// sharing at batch > 1).  fp8 e4m3fn and e2m1 codes are widened to bf16 exactly with gfx950's
+// scaled conversions and multiplied with two-wide bf16 dot products (gate/up) or widened to
+// fp32 (down); block scales are applied per 16-byte chunk (gate/up) or per block of rows
+// (down).
 #include "moe_dev.h"
 
 namespace moe {

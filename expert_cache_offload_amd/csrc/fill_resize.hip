@@ -9,9 +9,10 @@
 //
 // Gfx950 design: the copy is a kernel that reads the pinned pool through its device mapping
 // (zero-copy over PCIe) and writes the slot in HBM.  Its source and destination come from the
-// plan in device memory, so no host round trip is needed and the whole step can be captured in
-// a hipGraph; on the MI355X machine such a kernel with 256 workgroups moves 9 MiB blobs at the
-// link's full rate (measured 57.4 GB/s versus 54.2 GB/s for hipMemcpyAsync of the same blobs).
+// plan in device memory (the step plan, or the prefetch plan of the next layer), so no host
+// round trip is needed and the whole step can be captured in a hipGraph; 32 workgroups move
+// 9 MiB blobs at the link's full rate (55-57 GB/s against 53-54 GB/s for pinned
+// hipMemcpyAsync of the same blobs) and leave the rest of the GPU to concurrent kernels.
 //
 // Resize: FreeToken paper summary, execution-layer paragraph (cache rebuilt at a scheduler
 // safe point when the VRAM budget changes, without restarting) and problem paragraph (budgets

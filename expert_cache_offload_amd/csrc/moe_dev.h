@@ -5,12 +5,14 @@
 //   stamp[max_capacity]   global step of the slot's last use, -1 empty
 //   slot_of[L*E]          slot of each key, -1 when not cached
 //   ctrl[16]              occupancy n, capacity C, step counter, error bits, tickets
-//   stats[4]              steps, hits, misses, bytes filled
+//   stats[8]              steps, hits, misses, bytes filled, FFN bytes, CPU misses, ...
 // Per-step plan (rewritten by every route launch):
 //   hdr[16], U/u_slot/u_hit/hit_list/miss_list/miss_key/miss_slot/miss_victim[umax],
 //   count[umax], offset[umax+1], perm/inv_pos/tk_idx/tk_w[amax], logits[tdec*E],
-//   FFN intermediates (act) and per-expert outputs (yexp); for steps of more than eight
-//   tokens the block counts and offsets of the router and bf16 / fp32 row buffers.
+//   FFN intermediates (act) and per-expert outputs (yexp), the hybrid decode's CPU rows and
+//   keys; for steps of more than eight tokens the block counts and offsets of the router,
+//   bf16 / fp32 row buffers and the prefetch plan.
+// Host memory of a hybrid handle: the mailbox (HybMail, below) the route kernel posts to.
 #pragma once
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>

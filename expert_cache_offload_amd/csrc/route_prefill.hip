@@ -2,14 +2,18 @@
 //
 // The same plan as at decode (FreeToken paper summary, execution-layer paragraph: routing
 // dedup, hit classification and LRU victim selection on the GPU with no host round trip),
-// over a chunk whose routing union covers nearly every expert ("FreeToken：在消费级 NVIDIA
-// GPU 上进行 MoE 推理", section on the prefill union crossing PCIe).
+// over a chunk whose routing union covers nearly every expert (same page, problem
+// paragraph).  A fourth kernel plans the prefetch of the next layer (every expert of it, the
+// step before protected from eviction), whose fills then overlap this layer's FFN
+// ("FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理", "FreeToken 解决的问题": experts are
+// streamed ahead so that transfers overlap compute).
 //
 // Gfx950 design, three launches:
 //   router/top-k  - a workgroup owns 64 tokens: their router logits (fp64 accumulation of
 //                   exact bf16 x bf16 products, operands staged through LDS in 64-wide
-//                   contraction chunks, the next chunk's loads in flight) stay in LDS; one lane per token keeps its top-k
-//                   list (ties to the lower expert id) and the renormalised softmax
+//                   contraction chunks, the next chunk's loads in flight) stay in LDS; one
+//                   lane per token keeps its top-k list (ties to the lower expert id) and the
+//                   renormalised softmax
 //                   weights; an LDS bitmask per expert gives each (token, choice) its rank
 //                   among the block's tokens routed to the same expert, and the block's
 //                   per-expert counts;

@@ -219,8 +219,9 @@ moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int32_t* stamp,
                               int32_t* capacity);
 
 /* Prefetch mode for steps of more than 8 tokens (prefill chunks), whose routing union
- * covers nearly every expert ("FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理", on the prefill
- * union crossing PCIe): each moe_layer_step of layer l (l + 1 < layers) also plans a
+ * covers nearly every expert (FreeToken paper summary, agihunt.info / arXiv 2608.16157,
+ * problem paragraph), streaming experts ahead so that transfers overlap compute
+ * ("FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理", "FreeToken 解决的问题"): each moe_layer_step of layer l (l + 1 < layers) also plans a
  * prefetch step of layer l + 1 - an LRU step whose distinct set is every expert of l + 1,
  * with the slots of step l protected from eviction, taking its own step-counter value - and
  * copies its misses on fill_stream while step l's FFN runs; step l + 1's FFN waits for

@@ -31,9 +31,10 @@ R8  prefetch (steps of many tokens only): before layer l' is routed, a prefetch 
     layer l' is an R1-R6 step whose U is every expert of l', except that the victims also
     skip the keys of a protected set (the distinct keys of the layer step just before it,
     whose expert FFN may still be reading their slots).  It takes its own value of the
-    step counter.  (FreeToken：在消费级 NVIDIA GPU 上进行 MoE 推理, on the prefill union:
-    a long prefill routes to nearly every expert of every layer, so layer l' can be
-    fetched while layer l computes.)
+    step counter.  (FreeToken paper summary, problem paragraph: a long prefill's routing
+    union covers nearly every expert of every layer; "FreeToken：在消费级 NVIDIA GPU 上进行
+    MoE 推理", "FreeToken 解决的问题": experts are streamed ahead so that transfers overlap
+    compute - so layer l' can be fetched while layer l computes.)
 R9  hybrid decode (CPU in-place compute of some misses): of the step's m misses, in
     ascending expert id, the first m - q are filled as R3-R6 and the last q are computed
     by the CPU straight from the host pool: they take no slot, evict nothing and are not
