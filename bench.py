@@ -8,9 +8,10 @@ pinned host pool (58 GB), one LRU slot cache shared by all layers holding 30% of
 decode token through all 48 layer steps (route, dedup, classify, LRU, fills, FFN).  The
 first --warmup tokens are untimed; exactly --steps tokens are timed.
 
-Reported (one JSON line): decode tokens/s of the stack; the dominant FFN kernel (the
-gate/up weight-streaming kernel, two thirds of the expert bytes) against the MI355X HBM
-roofline - achieved = the expert-weight bytes it was given / its launch durations, timed
+Reported (one JSON line): decode tokens/s of the stack; the dominant FFN kernel against the
+MI355X HBM roofline (at one token with bf16 weights the fused gate/up + down kernel, which
+streams whole blobs; otherwise the gate/up kernel, two thirds of the expert bytes) -
+achieved = the expert-weight bytes it was given / its launch durations, timed
 with event pairs on the compute stream over the timed tokens; fill bandwidth against pinned
 hipMemcpyAsync H2D measured on the same box; the float64 CPU oracle on a bounded sample of
 the same workload.  A short untimed pass after the timed tokens times the other kernels
@@ -163,18 +164,18 @@ def _with_cache_frac(wl, frac: float):
 GATE_UP_END = "// ---------------------------------------------------------------- down role"
 
 
-def _ffn_source_hash() -> str:
-    """Hash of the decode FFN source up to the down role: the gate/up kernel and everything it
-    uses (formats, entry resolution); the down and combine kernels that follow do not change
-    the gate/up kernel's traffic."""
+def _ffn_source_hash(kernel: str = "ffn_gate_up_kernel") -> str:
+    """Hash of the decode FFN source a kernel's traffic depends on: for the gate/up kernel the
+    source up to the down role (formats, entry resolution, the gate/up role; the down and
+    combine kernels that follow do not change its traffic), for the fused kernel the file."""
     here = os.path.dirname(os.path.abspath(__file__))
     p = os.path.join(here, "expert_cache_offload_amd", "csrc", "ffn_decode.hip")
     text = open(p, "rb").read()
-    cut = text.find(GATE_UP_END.encode())
+    cut = text.find(GATE_UP_END.encode()) if kernel == "ffn_gate_up_kernel" else -1
     return hashlib.sha256(text[:cut] if cut > 0 else text).hexdigest()[:16]
 
 
-def _traffic_ratio_from_profile(name: str) -> float | None:
+def _traffic_ratio_from_profile(name: str, kernel: str = "ffn_gate_up_kernel") -> float | None:
     """HBM bytes per algorithmic byte of the gate/up kernel from a committed counter summary,
     if it was taken on the current kernel source (its header line records the source hash).
     The counters are taken with every launch streaming the same number of experts; the bench
@@ -183,7 +184,7 @@ def _traffic_ratio_from_profile(name: str) -> float | None:
     p = os.path.join(here, "profiles", name)
     if not os.path.exists(p):
         return None
-    h = _ffn_source_hash()
+    h = _ffn_source_hash(kernel)
     val = None
     src_ok = False
     for line in open(p):
@@ -557,11 +558,14 @@ def main() -> None:
         gu_bytes = prof["gate_up_timed_bytes"]  # expert bytes the timed launches were given
         gu_s = gu["ms"] / 1e3
         achieved = gu_bytes / gu_s / 1e9 if gu_s > 0 else 0.0
-        ratio = _traffic_ratio_from_profile(f"ffn_gate_up_{wl.name}_pmc.txt")
+        fused = gu_bytes > 0 and prof["fused_timed_bytes"] == gu_bytes
+        kname = "ffn_fused_kernel" if fused else "ffn_gate_up_kernel"
+        ratio = _traffic_ratio_from_profile(
+            f"{'ffn_fused' if fused else 'ffn_gate_up'}_{wl.name}_pmc.txt", kname)
         traffic = round(ratio * gu_bytes / max(1, gu["launches"])) if ratio else None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": traffic, "kernel": "ffn_gate_up_kernel",
+                    "traffic": traffic, "kernel": kname,
                     "launches": gu["launches"],
                     "avg_launch_us": round(gu["ms"] * 1e3 / max(1, gu["launches"]), 3),
                     "algorithmic_bytes_per_launch": round(gu_bytes / max(1, gu["launches"]))}

@@ -61,7 +61,7 @@ class MoeCounters(ctypes.Structure):
 class MoeProfile(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64 * 4), ("ms", ctypes.c_double * 4),
                 ("fill_bytes", ctypes.c_int64), ("ffn_weight_bytes", ctypes.c_int64),
-                ("gate_up_timed_bytes", ctypes.c_int64)]
+                ("gate_up_timed_bytes", ctypes.c_int64), ("fused_timed_bytes", ctypes.c_int64)]
 
 
 PROF_ROUTE, PROF_FILL, PROF_GATE_UP, PROF_DOWN = 1, 2, 4, 8
@@ -331,6 +331,7 @@ def moe_profile_read(handle: int) -> dict:
     out["fill_bytes"] = int(p.fill_bytes)
     out["ffn_weight_bytes"] = int(p.ffn_weight_bytes)
     out["gate_up_timed_bytes"] = int(p.gate_up_timed_bytes)
+    out["fused_timed_bytes"] = int(p.fused_timed_bytes)
     return out
 
 

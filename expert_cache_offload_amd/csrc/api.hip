@@ -28,6 +28,7 @@ hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const v
 int decode_ntok(int T);
 int down_columns_per_block(int fmt);
 int down_row_splits(int inter);
+int fused_row_blocks(const Dims& d);
 hipError_t launch_fill(const Dev& v, const void* pool_dev, void* arena, long long S, int group,
                        int ngroups, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
                        int prefetch, int E);
@@ -61,7 +62,7 @@ enum class State { Idle, Planned, Filled };
 struct Layout {
   size_t key_of, stamp, slot_of, ctrl, stats, hdr, U, u_slot, u_hit, hit_list, miss_list,
       miss_key, miss_slot, miss_victim, count, offset, perm, inv_pos, tk_idx, tk_w, logits,
-      act, act_shared, yexp, yexp_shared, ent, row_tok, row_w, moves, blk_cnt, blk_off, brank,
+      act, act_shared, yexp, yexp_shared, yfus, ent, row_tok, row_w, moves, blk_cnt, blk_off, brank,
       pact, pact_shared, pyexp, pyexp_shared, pf_hdr, pf_list, pf_ent, row_cpu, cpu_key, total;
 };
 
@@ -86,6 +87,7 @@ Dims make_dims(const moe_shape& s, int max_capacity) {
   d.max_capacity = max_capacity;
   d.RS = down_row_splits(s.inter);
   d.S = s.blob_bytes;
+  d.RSF = fused_row_blocks(d);
   return d;
 }
 
@@ -123,6 +125,7 @@ Layout make_layout(const Dims& d) {
   L.act_shared = take(d.has_shared ? sizeof(float) * (size_t)d.tdec * d.I : 256);
   L.yexp = take(sizeof(float) * (size_t)d.adec * d.RS * d.H);
   L.yexp_shared = take(d.has_shared ? sizeof(float) * (size_t)d.tdec * d.RS * d.H : 256);
+  L.yfus = take(d.RSF > 0 ? sizeof(float) * (size_t)d.K * d.RSF * d.H : 256);
   L.ent = take(sizeof(int) * 4 * (size_t)d.umax);
   L.row_tok = take(I4 * d.amax);
   L.row_w = take(sizeof(float) * d.amax);
@@ -173,6 +176,7 @@ Dev make_dev(void* ws, const Layout& L) {
   v.act_shared = (float*)(b + L.act_shared);
   v.yexp = (float*)(b + L.yexp);
   v.yexp_shared = (float*)(b + L.yexp_shared);
+  v.yfus = (float*)(b + L.yfus);
   v.ent = (int4*)(b + L.ent);
   v.row_tok = (int*)(b + L.row_tok);
   v.row_w = (float*)(b + L.row_w);
@@ -967,9 +971,13 @@ moe_status moe_profile_read(moe_cache c, moe_profile* out) {
   }
   out->fill_bytes = (int64_t)(st[STAT_BYTES] - P.stats0[STAT_BYTES]);
   out->ffn_weight_bytes = (int64_t)(st[STAT_FFN_BYTES] - P.stats0[STAT_FFN_BYTES]);
-  // the gate/up rows and their scales are exactly two thirds of a blob in every format
+  // the gate/up rows and their scales are exactly two thirds of a blob in every format; a
+  // fused one-token launch reads the whole blob
+  out->fused_timed_bytes =
+      (int64_t)(st[STAT_TIMED_FUSED_BYTES] - P.stats0[STAT_TIMED_FUSED_BYTES]);
   out->gate_up_timed_bytes =
-      (int64_t)((st[STAT_TIMED_BLOB_BYTES] - P.stats0[STAT_TIMED_BLOB_BYTES]) / 3 * 2);
+      (int64_t)((st[STAT_TIMED_BLOB_BYTES] - P.stats0[STAT_TIMED_BLOB_BYTES]) / 3 * 2) +
+      out->fused_timed_bytes;
   return MOE_OK;
 }
 

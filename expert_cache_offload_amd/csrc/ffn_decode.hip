@@ -22,6 +22,12 @@
 //              expert's output columns (fp32);
 //   combine  - y[t] = bf16(sum over the token's k experts' row splits, + the CPU experts'
 //              sum in hybrid decode, + the shared expert) in a fixed order.
+// At one token with bf16 weights and no shared expert (the batch-1 decode of the bf16
+// models) one fused kernel replaces gate/up and down: a workgroup owns 16 intermediate rows
+// of an expert, computes their activations and multiplies them straight into its 16 rows of
+// WdT, writing one fp32 partial of the output per row block; a wider combine adds them.  One
+// launch then streams every blob of the step, which halves the fixed launch and dependency
+// cost per byte; the partials cost 4% more HBM traffic than the activations they replace.
 // Kernel boundaries carry the dependencies: on gfx950 an agent-scope release / acquire per
 // workgroup is an L2 write-back / invalidate, far costlier than a second launch.
 // The route kernel publishes a packed entry table (slot, token count, first row, miss
@@ -679,6 +685,175 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
   a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(s);
 }
 
+// ---------------------------------------------------------------- fused one-token role
+// At one token (bf16 weights, no shared expert) the gate/up and down rows of an expert's
+// intermediate block run in one workgroup, so a single launch streams every blob of the step
+// and no activation row leaves the chip.  The workgroup owns FR = 16 intermediate rows: each
+// of its 8 waves computes the gate and up sums of two rows as in the gate/up role, the 16
+// activations meet in LDS, and the workgroup multiplies them into its 16 rows of WdT for every
+// output column.  Thread (column chunk cc, row group rg) holds NR rows of 8 columns; the
+// FR / NR row groups are added in LDS in a fixed order and the workgroup writes one fp32
+// partial per (expert row, row block).  Every weight load of the workgroup - its gate/up
+// chunks and its WdT rows - is issued before the first product.  The combine adds the
+// I / FR partials of each of the token's experts.
+constexpr int FFT = 512;  // threads per fused workgroup (8 waves)
+constexpr int FR = 16;    // intermediate rows per fused workgroup (two per wave)
+constexpr int kMaxPartialsF = 1024;  // top_k * I / FR, checked on the host
+
+template <int NR>
+__device__ void fused_role(const FfnArgs& a, const Entry& en, int rb, u32x4v (&xr)[GN][1],
+                           float* s_a, float* s_red) {
+  const Dims& d = a.d;
+  const int H = d.H, I = d.I;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (rb == 0 && tid == 0) {
+    atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
+    if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_FUSED_BYTES], (unsigned long long)d.S);
+  }
+  const float wt = en.shared ? 1.0f : a.v.row_w[en.row0];
+  const int i0 = rb * FR + wave, i1 = i0 + FR / 2;
+  const size_t hbytes = 2 * (size_t)H, rbytes = 2 * hbytes;  // bf16 half-row, gate|up row
+  const unsigned char* r0 = en.blob + (size_t)i0 * rbytes;
+  const unsigned char* r1 = en.blob + (size_t)i1 * rbytes;
+  const int ngq = H / 8;  // 16-byte chunks per half-row and per WdT row
+  const int cc = tid % ngq, rg = tid / ngq;
+  const unsigned char* wdt =
+      en.blob + (size_t)I * rbytes + (size_t)(rb * FR + rg * NR) * hbytes + (size_t)cc * 16;
+  float g0 = 0.f, u0 = 0.f, g1 = 0.f, u1 = 0.f;
+  u32x4v wd[NR];
+  for (int kb = 0; kb * 64 < ngq; kb += GN) {
+    u32x4v wg0[GN], wu0[GN], wg1[GN], wu1[GN];
+#pragma unroll
+    for (int k = 0; k < GN; ++k) {
+      int c = (kb + k) * 64 + lane;
+      c = c < ngq ? c : ngq - 1;  // in-row address; masked below
+      wg0[k] = *(const u32x4v*)(r0 + (size_t)c * 16);
+      wu0[k] = *(const u32x4v*)(r0 + hbytes + (size_t)c * 16);
+      wg1[k] = *(const u32x4v*)(r1 + (size_t)c * 16);
+      wu1[k] = *(const u32x4v*)(r1 + hbytes + (size_t)c * 16);
+    }
+    if (kb == 0) {  // the WdT rows go out behind the first pass, before any product
+#pragma unroll
+      for (int r = 0; r < NR; ++r) wd[r] = *(const u32x4v*)(wdt + (size_t)r * hbytes);
+    } else {
+      load_x1<FMT_BF16>(a, kb, lane, xr);
+    }
+#pragma unroll
+    for (int k = 0; k < GN; ++k) {
+      if ((kb + k) * 64 + lane < ngq) {
+        const uint32_t xw[4] = {xr[k][0].x, xr[k][0].y, xr[k][0].z, xr[k][0].w};
+        const uint32_t ag0[4] = {wg0[k].x, wg0[k].y, wg0[k].z, wg0[k].w};
+        const uint32_t au0[4] = {wu0[k].x, wu0[k].y, wu0[k].z, wu0[k].w};
+        const uint32_t ag1[4] = {wg1[k].x, wg1[k].y, wg1[k].z, wg1[k].w};
+        const uint32_t au1[4] = {wu1[k].x, wu1[k].y, wu1[k].z, wu1[k].w};
+        g0 = wdot<4>(ag0, xw, g0);
+        u0 = wdot<4>(au0, xw, u0);
+        g1 = wdot<4>(ag1, xw, g1);
+        u1 = wdot<4>(au1, xw, u1);
+      }
+    }
+  }
+  float gv[2] = {g0, g1}, uv[2] = {u0, u1};
+  wave_reduce_units<1>(gv, uv, lane);
+  if ((lane & 31) == 0)  // lane 0 holds row i0, lane 32 row i1
+    s_a[lane == 0 ? wave : wave + FR / 2] = silu(gv[0]) * uv[0] * wt;
+  __syncthreads();
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float ar = s_a[rg * NR + r];
+    float f[8];
+    unpack_d<FMT_BF16>(wd[r], f);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += ar * f[c];
+  }
+  float* out = a.v.yfus + ((size_t)en.row0 * d.RSF + rb) * H;
+  constexpr int RG = FR / NR;  // row groups (FFT / ngq)
+  if constexpr (RG == 1) {
+    *(float4*)(out + cc * 8) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *(float4*)(out + cc * 8 + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  } else {
+    *(float4*)(s_red + (size_t)rg * H + cc * 8) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *(float4*)(s_red + (size_t)rg * H + cc * 8 + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    __syncthreads();
+    for (int c = tid; c < H; c += FFT) {
+      float s = 0.f;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) s += s_red[(size_t)g * H + c];
+      out[c] = s;
+    }
+  }
+}
+
+// Combine of the fused partials: y[t] = bf16( sum over the token's experts and row blocks
+// + y_cpu[t] ).  A workgroup owns 64 columns of one token; thread (partial lane pl, column
+// quad cq) adds every 16th partial with 16-byte loads, all of them in flight at once; the 16
+// partial lanes are added in LDS in a fixed order.
+constexpr int CFP = 24;  // partials per thread per round
+
+__device__ void combine_fused_role(const FfnArgs& a, int cblk) {
+  const Dims& d = a.d;
+  const Dev& v = a.v;
+  const int per_tok = d.H / 64;
+  const int t = cblk / per_tok, c0 = (cblk % per_tok) * 64;
+  const int RSF = d.RSF, nrouted = d.K * RSF;
+  __shared__ int s_row[kMaxPartialsF];
+  __shared__ __align__(16) float s_sum[16 * 64];
+  __shared__ int s_ok;
+  const int ncpu = __hip_atomic_load(&v.hdr[HDR_NCPU], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = threadIdx.x; i < nrouted; i += FT) {
+    const int j = i / RSF, r = i - j * RSF;
+    const int pos = v.inv_pos[t * d.K + j];
+    s_row[i] = ncpu > 0 && v.row_cpu[pos] ? -1 : pos * RSF + r;
+  }
+  if (ncpu > 0 && threadIdx.x == 0) {
+    // the host's answer to this step, bounded as in the two-kernel combine
+    const long long step =
+        (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = true;
+#pragma nounroll
+    while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)v.hyb_timeout_ticks) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    s_ok = ok;
+    if (!ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
+  }
+  __syncthreads();
+  const int cq = threadIdx.x & 15, pl = threadIdx.x >> 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int base = pl; base < nrouted; base += 16 * CFP) {
+    int row[CFP];
+    float4 pv[CFP];
+#pragma unroll
+    for (int q = 0; q < CFP; ++q) row[q] = base + 16 * q < nrouted ? s_row[base + 16 * q] : -1;
+#pragma unroll
+    for (int q = 0; q < CFP; ++q)
+      pv[q] = *(const float4*)(v.yfus + (size_t)(row[q] < 0 ? 0 : row[q]) * d.H + c0 + cq * 4);
+#pragma unroll
+    for (int q = 0; q < CFP; ++q)
+      if (row[q] >= 0) {
+        s.x += pv[q].x; s.y += pv[q].y; s.z += pv[q].z; s.w += pv[q].w;
+      }
+  }
+  *(float4*)(s_sum + pl * 64 + cq * 4) = s;
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int c = c0 + threadIdx.x;
+  float y = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) y += s_sum[p * 64 + threadIdx.x];
+  if (ncpu > 0 && s_ok) {
+    const float* yc = (const float*)((const unsigned char*)v.mail + mail_y_offset(d.H));
+    y += __hip_atomic_load(yc + (size_t)t * d.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  a.y[(size_t)t * d.H + c] = f32_to_bf16_rne(y);
+}
+
 template <int FMT>
 static constexpr int down_hc() {
   return DTC * Fmt<FMT>::DC;
@@ -713,6 +888,65 @@ __global__ __launch_bounds__(FT) void ffn_down_kernel(FfnArgs a) {
 }
 
 __global__ __launch_bounds__(FT) void combine_kernel(FfnArgs a) { combine_role(a, blockIdx.x); }
+
+template <int NR>
+__global__ __launch_bounds__(FFT) void ffn_fused_kernel(FfnArgs a) {
+  __shared__ float s_a[FR];
+  extern __shared__ __align__(16) unsigned char smem[];  // row-group sums: (FR / NR) * H fp32
+  const int nrb = a.d.I / FR;
+  u32x4v xr[GN][1];
+  // the activations do not depend on the plan: they go out before the entry
+  load_x1<FMT_BF16>(a, 0, threadIdx.x & 63, xr);
+  Entry en;
+  if (!resolve(a, blockIdx.x / nrb, en)) return;  // uniform per workgroup
+  fused_role<NR>(a, en, blockIdx.x % nrb, xr, s_a, (float*)smem);
+}
+
+__global__ __launch_bounds__(FT) void combine_fused_kernel(FfnArgs a) {
+  combine_fused_role(a, blockIdx.x);
+}
+
+// Row blocks of the fused one-token FFN for this shape, or 0 when the shape takes the
+// gate/up + down kernels: bf16 weights without a shared expert, H / 8 chunks per row that
+// divide the 512 threads with FR * (H / 8) / 512 in {1, 2, 4, 8, 16} rows per thread, and at
+// most kMaxPartialsF partials per output.
+int fused_row_blocks(const Dims& d) {
+  if (d.fmt != FMT_BF16 || d.has_shared || d.I % FR != 0 || d.H % 64 != 0) return 0;
+  const int ngq = d.H / 8;
+  if (ngq > FFT || FFT % ngq != 0) return 0;
+  const int nr = FR * ngq / FFT;
+  if (nr < 1 || (nr & (nr - 1)) != 0 || nr > 16) return 0;
+  if (d.K * (d.I / FR) > kMaxPartialsF) return 0;
+  return d.I / FR;
+}
+
+template <int NR>
+static hipError_t launch_fused_nr(const FfnArgs& a, int grid, hipStream_t s, hipEvent_t e0,
+                                  hipEvent_t e1) {
+  return launch_timed(ffn_fused_kernel<NR>, dim3(grid), dim3(FFT), sizeof(float) * FFT * 8, s,
+                      e0, e1, a);
+}
+
+// stage 0: the fused kernel over the launch's entries; stage 1: the combine (when a.NC > 0)
+static hipError_t launch_fused(const FfnArgs& a, int stage, hipStream_t s, hipEvent_t e0,
+                               hipEvent_t e1) {
+  const Dims& d = a.d;
+  const int grid = stage == 0 ? a.NE * d.RSF : (a.NC > 0 ? a.T * (d.H / 64) : 0);
+  if (grid <= 0) {  // nothing to run; keep the timing events valid
+    hipError_t e = e0 ? hipEventRecord(e0, s) : hipSuccess;
+    if (e == hipSuccess && e1) e = hipEventRecord(e1, s);
+    return e;
+  }
+  if (stage == 1)
+    return launch_timed(combine_fused_kernel, dim3(grid), dim3(FT), 0, s, e0, e1, a);
+  switch (FR * (d.H / 8) / FFT) {
+    case 1: return launch_fused_nr<1>(a, grid, s, e0, e1);
+    case 2: return launch_fused_nr<2>(a, grid, s, e0, e1);
+    case 4: return launch_fused_nr<4>(a, grid, s, e0, e1);
+    case 8: return launch_fused_nr<8>(a, grid, s, e0, e1);
+    default: return launch_fused_nr<16>(a, grid, s, e0, e1);
+  }
+}
 
 int decode_ntok(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
@@ -788,6 +1022,7 @@ hipError_t launch_ffn_decode(const Dims& d, const Dev& v, const void* x, const v
             (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
             max_entries > 0 ? max_entries : 0, nc, e0 != nullptr};
   const int ntok = decode_ntok(T);
+  if (ntok == 1 && d.RSF > 0) return launch_fused(a, stage, s, e0, e1);
   switch (d.fmt) {
     case FMT_BF16: return launch_fmt<FMT_BF16>(a, ntok, stage, s, e0, e1);
     case FMT_FP8: return launch_fmt<FMT_FP8>(a, ntok, stage, s, e0, e1);

@@ -62,6 +62,7 @@ enum : int {
   STAT_FFN_BYTES = 4,
   STAT_TIMED_BLOB_BYTES = 5,  // blobs read by gate/up launches bracketed by timing events
   STAT_CPU = 6,               // misses computed in place by the CPU
+  STAT_TIMED_FUSED_BYTES = 7, // blobs read by fused one-token FFN launches bracketed by events
   STAT_WORDS = 8
 };
 
@@ -78,6 +79,7 @@ struct Dims {
   int nblk;          // 64-token blocks of the many-token path (0 when max_tokens <= 8)
   int max_capacity;  // slots the arena holds
   int RS;            // row splits of the decode down projection
+  int RSF;           // row blocks of the fused one-token FFN (0: the shape takes two kernels)
   long long S;       // blob bytes
 };
 
@@ -135,6 +137,7 @@ struct Dev {
   float* act_shared;   // [tdec][I] shared expert (decode)
   float* yexp;         // [adec][RS][H] per (expert, token) output (decode)
   float* yexp_shared;  // [tdec][RS][H] shared expert (decode)
+  float* yfus;         // [K][RSF][H] fused one-token FFN partials per (expert row, row block)
   int* blk_cnt;        // [nblk][E] assignments per (64-token block, expert)
   int* blk_off;        // [nblk][E] first expert-sorted row of each (block, expert)
   int* brank;          // [amax] rank of a (token, choice) among its block's rows

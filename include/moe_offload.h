@@ -292,12 +292,14 @@ moe_status moe_stats(moe_cache cache, moe_counters* out);
 /* Per-kernel timing of the library's own launches, for measurement.  One launch in every
  * `every` (>= 1) of each kind selected in `mask` is bracketed by a pair of timing events on
  * the stream it runs on (eager calls only: do not enable while a stream is captured).  A
- * timing event costs queue time, so sampling keeps the timed run close to an untimed one.  Kinds: route/plan kernel,
- * fill kernel, FFN gate/up kernel, FFN down kernel (with the combine when it follows).
+ * timing event costs queue time, so sampling keeps the timed run close to an untimed one.
+ * Kinds: route/plan kernel, fill kernel, first FFN stage (the gate/up kernel, or at one token
+ * with bf16 weights and no shared expert the fused gate/up + down kernel), second FFN stage
+ * (the down kernel with the combine when it follows; after a fused launch the combine alone).
  * moe_profile_enable resets the accumulators (mask 0 switches timing off); moe_profile_read
  * synchronises.  ffn_weight_bytes counts the expert-weight bytes the FFN kernels were given
  * (each processed expert blob once): the algorithmic bytes of the FFN, of which the gate/up
- * kernel reads exactly two thirds in every weight format. */
+ * kernel reads exactly two thirds in every weight format and the fused kernel all. */
 #define MOE_PROF_ROUTE 1
 #define MOE_PROF_FILL 2
 #define MOE_PROF_GATE_UP 4
@@ -307,7 +309,10 @@ typedef struct {
   int64_t launches[4]; /* route, fill, gate/up, down */
   double ms[4];        /* summed event-pair durations, same order */
   int64_t fill_bytes, ffn_weight_bytes;
-  int64_t gate_up_timed_bytes; /* algorithmic bytes of the timed gate/up launches */
+  int64_t gate_up_timed_bytes; /* algorithmic weight bytes of the timed first-stage FFN
+                                  launches: two thirds of each blob for the gate/up kernel,
+                                  the whole blob for the fused one-token kernel */
+  int64_t fused_timed_bytes;   /* the part of gate_up_timed_bytes read by fused launches */
 } moe_profile;
 
 moe_status moe_profile_enable(moe_cache cache, int32_t mask, int32_t every);
