@@ -23,11 +23,11 @@
 //   combine  - y[t] = bf16(sum over the token's k experts' row splits, + the CPU experts'
 //              sum in hybrid decode, + the shared expert) in a fixed order.
 // At one token with bf16 weights and no shared expert (the batch-1 decode of the bf16
-// models) one fused kernel replaces gate/up and down: a workgroup owns 16 intermediate rows
-// of an expert, computes their activations and multiplies them straight into its 16 rows of
+// models) one fused kernel replaces gate/up and down: a workgroup owns 8 intermediate rows
+// of an expert, computes their activations and multiplies them straight into its 8 rows of
 // WdT, writing one fp32 partial of the output per row block; a wider combine adds them.  One
 // launch then streams every blob of the step, which halves the fixed launch and dependency
-// cost per byte; the partials cost 4% more HBM traffic than the activations they replace.
+// cost per byte; the partials cost 8% more HBM traffic than the activations they replace.
 // Kernel boundaries carry the dependencies: on gfx950 an agent-scope release / acquire per
 // workgroup is an L2 write-back / invalidate, far costlier than a second launch.
 // The route kernel publishes a packed entry table (slot, token count, first row, miss
@@ -688,16 +688,17 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
 // ---------------------------------------------------------------- fused one-token role
 // At one token (bf16 weights, no shared expert) the gate/up and down rows of an expert's
 // intermediate block run in one workgroup, so a single launch streams every blob of the step
-// and no activation row leaves the chip.  The workgroup owns FR = 16 intermediate rows: each
-// of its 8 waves computes the gate and up sums of two rows as in the gate/up role, the 16
-// activations meet in LDS, and the workgroup multiplies them into its 16 rows of WdT for every
+// and no activation row leaves the chip.  The workgroup owns FR = 8 intermediate rows: each
+// of its 4 waves computes the gate and up sums of two rows as in the gate/up role, the 8
+// activations meet in LDS, and the workgroup multiplies them into its 8 rows of WdT for every
 // output column.  Thread (column chunk cc, row group rg) holds NR rows of 8 columns; the
 // FR / NR row groups are added in LDS in a fixed order and the workgroup writes one fp32
 // partial per (expert row, row block).  Every weight load of the workgroup - its gate/up
 // chunks and its WdT rows - is issued before the first product.  The combine adds the
 // I / FR partials of each of the token's experts.
-constexpr int FFT = 512;  // threads per fused workgroup (8 waves)
-constexpr int FR = 16;    // intermediate rows per fused workgroup (two per wave)
+constexpr int FR = 8;            // intermediate rows per fused workgroup (two per wave)
+constexpr int FFT = FR / 2 * 64;  // threads per fused workgroup
+constexpr int FWPE = 1;           // lower bound of waves per SIMD asked of the compiler
 constexpr int kMaxPartialsF = 1024;  // top_k * I / FR, checked on the host
 
 template <int NR>
@@ -786,19 +787,21 @@ __device__ void fused_role(const FfnArgs& a, const Entry& en, int rb, u32x4v (&x
 }
 
 // Combine of the fused partials: y[t] = bf16( sum over the token's experts and row blocks
-// + y_cpu[t] ).  A workgroup owns 64 columns of one token; thread (partial lane pl, column
-// quad cq) adds every 16th partial with 16-byte loads, all of them in flight at once; the 16
+// + y_cpu[t] ).  A workgroup owns 32 columns of one token; thread (partial lane pl, column
+// quad cq) adds every 32nd partial with 16-byte loads, CFP of them in flight at once; the 32
 // partial lanes are added in LDS in a fixed order.
-constexpr int CFP = 24;  // partials per thread per round
+constexpr int CFC = 32;         // output columns per combine workgroup
+constexpr int CFL = FT / (CFC / 4);  // partial lanes
+constexpr int CFP = 24;         // partials per thread per round
 
 __device__ void combine_fused_role(const FfnArgs& a, int cblk) {
   const Dims& d = a.d;
   const Dev& v = a.v;
-  const int per_tok = d.H / 64;
-  const int t = cblk / per_tok, c0 = (cblk % per_tok) * 64;
+  const int per_tok = d.H / CFC;
+  const int t = cblk / per_tok, c0 = (cblk % per_tok) * CFC;
   const int RSF = d.RSF, nrouted = d.K * RSF;
   __shared__ int s_row[kMaxPartialsF];
-  __shared__ __align__(16) float s_sum[16 * 64];
+  __shared__ __align__(16) float s_sum[CFL * CFC];
   __shared__ int s_ok;
   const int ncpu = __hip_atomic_load(&v.hdr[HDR_NCPU], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int i = threadIdx.x; i < nrouted; i += FT) {
@@ -824,13 +827,14 @@ __device__ void combine_fused_role(const FfnArgs& a, int cblk) {
     if (!ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
   }
   __syncthreads();
-  const int cq = threadIdx.x & 15, pl = threadIdx.x >> 4;
+  const int cq = threadIdx.x % (CFC / 4), pl = threadIdx.x / (CFC / 4);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = pl; base < nrouted; base += 16 * CFP) {
+  for (int base = pl; base < nrouted; base += CFL * CFP) {
     int row[CFP];
     float4 pv[CFP];
 #pragma unroll
-    for (int q = 0; q < CFP; ++q) row[q] = base + 16 * q < nrouted ? s_row[base + 16 * q] : -1;
+    for (int q = 0; q < CFP; ++q)
+      row[q] = base + CFL * q < nrouted ? s_row[base + CFL * q] : -1;
 #pragma unroll
     for (int q = 0; q < CFP; ++q)
       pv[q] = *(const float4*)(v.yfus + (size_t)(row[q] < 0 ? 0 : row[q]) * d.H + c0 + cq * 4);
@@ -840,13 +844,13 @@ __device__ void combine_fused_role(const FfnArgs& a, int cblk) {
         s.x += pv[q].x; s.y += pv[q].y; s.z += pv[q].z; s.w += pv[q].w;
       }
   }
-  *(float4*)(s_sum + pl * 64 + cq * 4) = s;
+  *(float4*)(s_sum + pl * CFC + cq * 4) = s;
   __syncthreads();
-  if (threadIdx.x >= 64) return;
+  if (threadIdx.x >= CFC) return;
   const int c = c0 + threadIdx.x;
   float y = 0.f;
 #pragma unroll
-  for (int p = 0; p < 16; ++p) y += s_sum[p * 64 + threadIdx.x];
+  for (int p = 0; p < CFL; ++p) y += s_sum[p * CFC + threadIdx.x];
   if (ncpu > 0 && s_ok) {
     const float* yc = (const float*)((const unsigned char*)v.mail + mail_y_offset(d.H));
     y += __hip_atomic_load(yc + (size_t)t * d.H + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -890,7 +894,7 @@ __global__ __launch_bounds__(FT) void ffn_down_kernel(FfnArgs a) {
 __global__ __launch_bounds__(FT) void combine_kernel(FfnArgs a) { combine_role(a, blockIdx.x); }
 
 template <int NR>
-__global__ __launch_bounds__(FFT) void ffn_fused_kernel(FfnArgs a) {
+__global__ __launch_bounds__(FFT, FWPE) void ffn_fused_kernel(FfnArgs a) {
   __shared__ float s_a[FR];
   extern __shared__ __align__(16) unsigned char smem[];  // row-group sums: (FR / NR) * H fp32
   const int nrb = a.d.I / FR;
@@ -908,14 +912,14 @@ __global__ __launch_bounds__(FT) void combine_fused_kernel(FfnArgs a) {
 
 // Row blocks of the fused one-token FFN for this shape, or 0 when the shape takes the
 // gate/up + down kernels: bf16 weights without a shared expert, H / 8 chunks per row that
-// divide the 512 threads with FR * (H / 8) / 512 in {1, 2, 4, 8, 16} rows per thread, and at
-// most kMaxPartialsF partials per output.
+// divide the FFT threads with FR * (H / 8) / FFT in {1, 2, 4, 8} rows per thread (at most FR),
+// and at most kMaxPartialsF partials per output.
 int fused_row_blocks(const Dims& d) {
   if (d.fmt != FMT_BF16 || d.has_shared || d.I % FR != 0 || d.H % 64 != 0) return 0;
   const int ngq = d.H / 8;
   if (ngq > FFT || FFT % ngq != 0) return 0;
   const int nr = FR * ngq / FFT;
-  if (nr < 1 || (nr & (nr - 1)) != 0 || nr > 16) return 0;
+  if (nr < 1 || (nr & (nr - 1)) != 0 || nr > 8 || nr > FR) return 0;
   if (d.K * (d.I / FR) > kMaxPartialsF) return 0;
   return d.I / FR;
 }
@@ -931,7 +935,7 @@ static hipError_t launch_fused_nr(const FfnArgs& a, int grid, hipStream_t s, hip
 static hipError_t launch_fused(const FfnArgs& a, int stage, hipStream_t s, hipEvent_t e0,
                                hipEvent_t e1) {
   const Dims& d = a.d;
-  const int grid = stage == 0 ? a.NE * d.RSF : (a.NC > 0 ? a.T * (d.H / 64) : 0);
+  const int grid = stage == 0 ? a.NE * d.RSF : (a.NC > 0 ? a.T * (d.H / CFC) : 0);
   if (grid <= 0) {  // nothing to run; keep the timing events valid
     hipError_t e = e0 ? hipEventRecord(e0, s) : hipSuccess;
     if (e == hipSuccess && e1) e = hipEventRecord(e1, s);
@@ -943,8 +947,7 @@ static hipError_t launch_fused(const FfnArgs& a, int stage, hipStream_t s, hipEv
     case 1: return launch_fused_nr<1>(a, grid, s, e0, e1);
     case 2: return launch_fused_nr<2>(a, grid, s, e0, e1);
     case 4: return launch_fused_nr<4>(a, grid, s, e0, e1);
-    case 8: return launch_fused_nr<8>(a, grid, s, e0, e1);
-    default: return launch_fused_nr<16>(a, grid, s, e0, e1);
+    default: return launch_fused_nr<8>(a, grid, s, e0, e1);
   }
 }
 
