@@ -260,8 +260,11 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
   const int ntiles = s_mt[n] * NT;
   const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;     // A: rows lr + 32 h
   // B: this thread's 4 consecutive contraction rows bk .. bk + 3, columns bc .. bc + 8, so the
-  // transpose into LDS is 8 stores of 4 contraction values (8 bytes) each
-  const int bk = (threadIdx.x >> 4) * 4, bc = (threadIdx.x & 15) * 8;
+  // transpose into LDS is 8 stores of 4 contraction values (8 bytes) each.  The 16 lanes of a
+  // wave that share a column block take the 16 contraction offsets: one store instruction then
+  // covers every bank once per column block (with lanes on columns 8 apart, 8 * LDK bf16 is a
+  // multiple of the bank count and 16 lanes would hit one bank).
+  const int bk = (threadIdx.x & 15) * 4, bc = (threadIdx.x >> 4) * 8;
   for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
