@@ -9,17 +9,19 @@
 // turning this overlap off at about a quarter of prefill speed).
 //
 // Gfx950 design.  Dense contractions on v_mfma_f32_32x32x16_bf16 (fp32 accumulation):
-//   gate/up  - tile = 128 rows x 64 intermediate rows; the 128 GEMM columns are the 64 gate
-//              rows and the 64 up rows, so each wave holds gate and up of the same
+//   gate/up  - tile = 128 rows x 128 intermediate rows; the 256 GEMM columns are the 128
+//              gate rows and the 128 up rows, so each wave holds gate and up of the same
 //              (row, i) in the same lane and the epilogue a = silu(g) * u * w is per lane;
-//              rows are gathered from x by the plan's row -> token map; a is stored bf16;
+//              a wave owns 64 rows x 64 intermediate rows (eight 32 x 32 MFMA tiles: six
+//              16-byte LDS reads feed eight MFMAs); rows are gathered from x by the plan's
+//              row -> token map; a is stored bf16;
 //   down     - tile = 128 rows x 128 output columns over the stored transpose WdT, whose
 //              rows are contraction rows: the B tile is transposed on its way into LDS;
 //              fp32 partial rows per (token, choice);
 //   combine  - y[t] = bf16(sum over the token's k rows (+ shared) in a fixed order).
-// Four waves per workgroup in a 2 x 2 arrangement (64 x 64 each: four 32 x 32 MFMA tiles),
-// a 32-wide contraction stage in LDS with the next stage's global loads in flight during
-// the MFMAs.  Workgroups are persistent over the launch's tiles, whose count depends on
+// Four waves per workgroup in a 2 x 2 arrangement (down: 64 x 64 each, four 32 x 32 MFMA
+// tiles), a 64-wide contraction stage in LDS with the next stage's global loads in flight
+// during the MFMAs.  Workgroups are persistent over the launch's tiles, whose count depends on
 // the plan (read on the device): a prefix over the launch's entries maps a tile to its
 // expert, row tile and column tile.
 #include "moe_dev.h"
@@ -34,7 +36,7 @@ constexpr int PFT = 256;        // threads (4 waves)
 constexpr int BM = 128;         // rows per tile
 constexpr int BK = 64;          // contraction per LDS stage (128-byte row segments)
 constexpr int LDK = BK + 8;     // padded LDS row (bf16): 144 bytes
-constexpr int GBI = 64;         // intermediate rows per gate/up tile
+constexpr int GBI = 128;        // intermediate rows per gate/up tile (256 GEMM columns)
 constexpr int DBN = 128;        // output columns per down tile
 constexpr int kMaxEntriesPf = 1040;
 
@@ -132,7 +134,8 @@ __device__ __forceinline__ int xcd_order() {
 __device__ __forceinline__ uint16_t pf_bf16(float f) { return f32_to_bf16_rne(f); }
 
 // ---------------------------------------------------------------- gate / up
-__global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
+// (two waves per SIMD: the accumulators and the stage's loads fit 256 registers per lane)
+__global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
   __shared__ __align__(16) uint16_t As[BM * LDK];
   __shared__ __align__(16) uint16_t Bs[2 * GBI * LDK];
   __shared__ int s_mt[kMaxEntriesPf + 1];
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
   const int n = pf_tile_prefix(a, s_mt, first);
   const int NT = I / GBI;
   const int ntiles = s_mt[n] * NT;
-  // this thread's 16-byte chunks of each stage: rows lr + 32 h (h < 4), columns lc .. lc + 8
+  // this thread's 16-byte chunks of each stage: A rows lr + 32 h (h < 4), B rows lr + 32 h
+  // (h < 8), columns lc .. lc + 8
   const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
   for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
@@ -171,73 +175,78 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_gate_up_kernel(PfArgs a) {
       const int tok = !aval[h] ? 0 : en.shared ? r : a.v.row_tok[en.row0 + r];
       arow[h] = a.x + (size_t)tok * H;
     }
-    // B rows: tile column c < 64 is gate row i0 + c, c >= 64 is up row i0 + c - 64
-    const uint16_t* brow[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int c = lr + 32 * h;
-      const int i = i0 + (c & 63);
-      brow[h] = (const uint16_t*)en.blob + (size_t)i * 2 * H + (c >= 64 ? H : 0);
-    }
-    f32x16_t acc[2][2];
+    // B rows: tile column c = lr + 32 h < GBI is gate row i0 + c, c >= GBI is up row
+    // i0 + c - GBI; one base pointer and workgroup-uniform offsets (h & 3) * 64 H + (h >> 2) H
+    const uint16_t* bbase = (const uint16_t*)en.blob + (size_t)(i0 + lr) * 2 * H;
+    f32x16_t acc[2][2][2];  // [row tile][gate, up][column tile]
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[rr][g][q] = 0.f;
-    u32x4_t ra[4], rb[4];
-    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
+          for (int q = 0; q < 16; ++q) acc[rr][g][cc][q] = 0.f;
+    u32x4_t ra[4], rb[8];
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
     // loads are unconditional (rows past the count read a valid row) and masked when they
     // are stored to LDS: a conditional load would make the compiler wait for it at once
-    for (int h = 0; h < 4; ++h) {
-      ra[h] = *(const u32x4_t*)(arow[h] + lc);
-      rb[h] = *(const u32x4_t*)(brow[h] + lc);
-    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) ra[h] = *(const u32x4_t*)(arow[h] + lc);
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      rb[h] = *(const u32x4_t*)(bbase + (size_t)((h & 3) * 64 + (h >> 2)) * H + lc);
     for (int k0 = 0; k0 < H; k0 += BK) {
       __syncthreads();  // the previous stage's MFMAs are done with the LDS tiles
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
+      for (int h = 0; h < 4; ++h)
         *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = aval[h] ? ra[h] : z4;
-        *(u32x4_t*)(Bs + (lr + 32 * h) * LDK + lc) = rb[h];
-      }
+#pragma unroll
+      for (int h = 0; h < 8; ++h) *(u32x4_t*)(Bs + (lr + 32 * h) * LDK + lc) = rb[h];
       __syncthreads();
       const int kn = k0 + BK < H ? k0 + BK : k0;  // last stage: harmless reload
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {  // next stage's loads overlap this stage's MFMAs
-        ra[h] = *(const u32x4_t*)(arow[h] + kn + lc);
-        rb[h] = *(const u32x4_t*)(brow[h] + kn + lc);
-      }
+      for (int h = 0; h < 4; ++h) ra[h] = *(const u32x4_t*)(arow[h] + kn + lc);
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        rb[h] = *(const u32x4_t*)(bbase + (size_t)((h & 3) * 64 + (h >> 2)) * H + kn + lc);
       __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
         const int ko = kk + 8 * (lane >> 5);
-        bf16x8_t af[2], bf[2];
+        bf16x8_t af[2], bf[2][2];
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
           af[rr] = *(const bf16x8_t*)(As + (wm * 64 + rr * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          bf[g] = *(const bf16x8_t*)(Bs + (g * 64 + wn * 32 + (lane & 31)) * LDK + ko);
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+            bf[g][cc] = *(const bf16x8_t*)(Bs + (g * GBI + wn * 64 + cc * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
           for (int g = 0; g < 2; ++g)
-            acc[rr][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[g], acc[rr][g], 0, 0, 0);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+              acc[rr][g][cc] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[g][cc], acc[rr][g][cc], 0, 0, 0);
       }
     }
-    // epilogue: lane holds column i = i0 + wn*32 + lane%32 for 16 rows of each row tile
-    const int i = i0 + wn * 32 + (lane & 31);
+    // epilogue: lane holds column i = i0 + wn*64 + cc*32 + lane%32 for 16 rows of each row tile
     uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int cc = 0; cc < 2; ++cc) {
+      const int i = i0 + wn * 64 + cc * 32 + (lane & 31);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        if (r < en.rows) {
-          const float val = pf_silu(acc[rr][0][q]) * acc[rr][1][q] * s_w[r - m0];
-          act[(size_t)(en.row0 + r) * I + i] = pf_bf16(val);
+      for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+          if (r < en.rows) {
+            const float val = pf_silu(acc[rr][0][cc][q]) * acc[rr][1][cc][q] * s_w[r - m0];
+            act[(size_t)(en.row0 + r) * I + i] = pf_bf16(val);
+          }
         }
       }
     }
@@ -371,7 +380,8 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_combine_kernel(PfArgs a) {
   a.y[(size_t)t * H + c] = f32_to_bf16_rne(s);
 }
 
-constexpr int kPfGrid = 768;  // persistent workgroups per GEMM launch (3 per CU: 40 KiB LDS each)
+constexpr int kPfGrid = 768;    // persistent down workgroups per launch (3 per CU: 40 KiB LDS each)
+constexpr int kPfGridGu = 512;  // persistent gate/up workgroups per launch (2 per CU: 59 KiB LDS each)
 
 // stage 0: gate/up; stage 1: down; stage 2: combine.  e0/e1 (nullable) time the launch.
 hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const void* arena,
@@ -381,7 +391,7 @@ hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const 
            (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
            e0 != nullptr};
   if (stage == 0)
-    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
+    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGridGu), dim3(PFT), 0, s, e0, e1, a);
   if (stage == 1)
     return launch_timed(ffn_prefill_down_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
   return launch_timed(ffn_prefill_combine_kernel, dim3(T * (d.H / PFT)), dim3(PFT), 0, s, e0, e1,
