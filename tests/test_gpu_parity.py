@@ -94,6 +94,19 @@ def test_bf16_decode_multilayer_evictions(groups):
     _log(f"bf16 4-layer: max rel-L2 {max(errs):.2e}")
 
 
+@pytest.mark.parametrize("hidden,inter,groups", [(512, 256, 0), (1024, 384, 2), (4096, 256, 0)])
+def test_bf16_one_token_hidden_sizes(hidden, inter, groups):
+    """bf16 decode at one token across hidden sizes: 512 and 1024 take the fused one-token
+    FFN with 2 and 4 WdT rows per thread (the workloads' 256 and 2048 take 1 and 8), 4096 the
+    gate/up and down kernels."""
+    wl = dataclasses.replace(mi.WORKLOADS["qwen35b_decode"], name=f"bf16_h{hidden}_i{inter}",
+                             layers=2, hidden=hidden, inter=inter, experts=32, token_steps=12)
+    _log(f"case {wl.name} groups={groups} C={wl.capacity}")
+    with _bench(wl, groups=groups) as wb:
+        errs = run_parity(wb, wl.token_steps)
+    _log(f"bf16 H={hidden}: max rel-L2 {max(errs):.2e}")
+
+
 @pytest.mark.parametrize("groups", [0, 3])
 def test_bf16_decode_eight_streams(groups):
     """8 decode streams batched at the 35B shape: one dedup and one cache step for 8 tokens,
