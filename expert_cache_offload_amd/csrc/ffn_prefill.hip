@@ -38,6 +38,7 @@ constexpr int BK = 64;          // contraction per LDS stage (128-byte row segme
 constexpr int LDK = BK + 8;     // padded LDS row (bf16): 144 bytes
 constexpr int GBI = 128;        // intermediate rows per gate/up tile (256 GEMM columns)
 constexpr int DBN = 128;        // output columns per down tile
+constexpr int DBM = 256;        // rows per down tile
 constexpr int kMaxEntriesPf = 1040;
 
 struct PfArgs {
@@ -96,13 +97,14 @@ __device__ __forceinline__ PfEntry pf_entry(const PfArgs& a, int g) {
   return en;
 }
 
-// Row tiles of the launch's entries: s_mt[j] = first row tile of entry j (exclusive prefix),
-// s_mt[n] = total.  Returns n.
+// Row tiles of TBM rows of the launch's entries: s_mt[j] = first row tile of entry j
+// (exclusive prefix), s_mt[n] = total.  Returns n.
+template <int TBM>
 __device__ int pf_tile_prefix(const PfArgs& a, int* s_mt, int& first) {
   const int n = pf_launch_entries(a, first);
   for (int j = threadIdx.x; j < n; j += PFT) {
     const PfEntry en = pf_entry(a, first + j);
-    s_mt[j + 1] = (en.rows + BM - 1) / BM;
+    s_mt[j + 1] = (en.rows + TBM - 1) / TBM;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int first;
-  const int n = pf_tile_prefix(a, s_mt, first);
+  const int n = pf_tile_prefix<BM>(a, s_mt, first);
   const int NT = I / GBI;
   const int ntiles = s_mt[n] * NT;
   // this thread's 16-byte chunks of each stage: A rows lr + 32 h (h < 4), B rows lr + 32 h
@@ -255,8 +257,11 @@ __global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
 }
 
 // ---------------------------------------------------------------- down
-__global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
-  __shared__ __align__(16) uint16_t As[BM * LDK];
+// Tile = 256 rows x 128 output columns; a wave owns 128 rows x 64 columns (eight 32 x 32 MFMA
+// tiles: six 16-byte LDS reads feed eight MFMAs), so every transposed WdT element in LDS
+// serves 256 rows.  Two workgroups (58 KiB LDS each) per CU.
+__global__ __launch_bounds__(PFT, 2) void ffn_prefill_down_kernel(PfArgs a) {
+  __shared__ __align__(16) uint16_t As[DBM * LDK];
   __shared__ __align__(16) uint16_t Bs[DBN * LDK];  // [column][contraction]
   __shared__ int s_mt[kMaxEntriesPf + 1];
   const Dims& d = a.d;
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int first;
-  const int n = pf_tile_prefix(a, s_mt, first);
+  const int n = pf_tile_prefix<DBM>(a, s_mt, first);
   const int NT = H / DBN;
   const int ntiles = s_mt[n] * NT;
   const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;     // A: rows lr + 32 h
@@ -278,38 +283,38 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
     const PfEntry en = pf_entry(a, first + j);
-    const int m0 = (mt - s_mt[j]) * BM;
+    const int m0 = (mt - s_mt[j]) * DBM;
     const int n0 = nt * DBN;
-    const uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
-    const uint16_t* arow[4];
-    bool aval[4];
+    const uint16_t* act = (en.shared ? a.v.pact_shared : a.v.pact) + (size_t)en.row0 * I;
+    // A rows: expert-sorted rows m0 + lr + 32 h; rows past the count read row 0 and are zeroed
+    int aoff[8];
+    unsigned amask = 0;  // bit h: row m0 + lr + 32 h exists
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < 8; ++h) {
       const int r = m0 + lr + 32 * h;
-      aval[h] = r < en.rows;
-      arow[h] = act + (size_t)(en.row0 + (aval[h] ? r : 0)) * I;
+      const bool ok = r < en.rows;
+      amask |= ok ? 1u << h : 0u;
+      aoff[h] = (ok ? r : 0) * I;
     }
     const uint16_t* wdt = (const uint16_t*)en.blob + (size_t)2 * I * H;  // WdT [I][H]
-    f32x16_t acc[2][2];
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[rr][cc][q] = 0.f;
-    u32x4_t ra[4], rb[4];
+    u32x4_t ra[8], rb[4];
     const u32x4_t z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      ra[h] = *(const u32x4_t*)(arow[h] + lc);
-      rb[h] = *(const u32x4_t*)(wdt + (size_t)(bk + h) * H + n0 + bc);
-    }
+    for (int h = 0; h < 8; ++h) ra[h] = *(const u32x4_t*)(act + aoff[h] + lc);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) rb[h] = *(const u32x4_t*)(wdt + (size_t)(bk + h) * H + n0 + bc);
     for (int k0 = 0; k0 < I; k0 += BK) {
       __syncthreads();
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = aval[h] ? ra[h] : z4;
-      }
+      for (int h = 0; h < 8; ++h)
+        *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = (amask >> h) & 1u ? ra[h] : z4;
       // transpose the 4 x 8 block: column c gets (row0, row1) and (row2, row3) packed pairs
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -322,23 +327,23 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
       __syncthreads();
       const int kn = k0 + BK < I ? k0 + BK : k0;  // last stage: harmless reload
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        ra[h] = *(const u32x4_t*)(arow[h] + kn + lc);
+      for (int h = 0; h < 8; ++h) ra[h] = *(const u32x4_t*)(act + aoff[h] + kn + lc);
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
         rb[h] = *(const u32x4_t*)(wdt + (size_t)(kn + bk + h) * H + n0 + bc);
-      }
       __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
 #pragma unroll
       for (int kk = 0; kk < BK; kk += 16) {
         const int ko = kk + 8 * (lane >> 5);
-        bf16x8_t af[2], bf[2];
+        bf16x8_t af[4], bf[2];
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-          af[rr] = *(const bf16x8_t*)(As + (wm * 64 + rr * 32 + (lane & 31)) * LDK + ko);
+        for (int rr = 0; rr < 4; ++rr)
+          af[rr] = *(const bf16x8_t*)(As + (wm * 128 + rr * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
           bf[cc] = *(const bf16x8_t*)(Bs + (wn * 64 + cc * 32 + (lane & 31)) * LDK + ko);
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
+        for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc)
             acc[rr][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[cc], acc[rr][cc], 0, 0, 0);
@@ -346,10 +351,10 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_down_kernel(PfArgs a) {
     }
     float* yrow = en.shared ? a.v.pyexp_shared : a.v.pyexp;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int r = m0 + wm * 128 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
         if (r < en.rows) {
           float* out = yrow + (size_t)(en.row0 + r) * H + n0 + wn * 64 + (lane & 31);
           out[0] = acc[rr][0][q];
@@ -380,8 +385,7 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_combine_kernel(PfArgs a) {
   a.y[(size_t)t * H + c] = f32_to_bf16_rne(s);
 }
 
-constexpr int kPfGrid = 768;    // persistent down workgroups per launch (3 per CU: 40 KiB LDS each)
-constexpr int kPfGridGu = 512;  // persistent gate/up workgroups per launch (2 per CU: 59 KiB LDS each)
+constexpr int kPfGrid = 512;  // persistent workgroups per GEMM launch (2 per CU: < 60 KiB LDS each)
 
 // stage 0: gate/up; stage 1: down; stage 2: combine.  e0/e1 (nullable) time the launch.
 hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const void* arena,
@@ -391,7 +395,7 @@ hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const 
            (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
            e0 != nullptr};
   if (stage == 0)
-    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGridGu), dim3(PFT), 0, s, e0, e1, a);
+    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
   if (stage == 1)
     return launch_timed(ffn_prefill_down_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
   return launch_timed(ffn_prefill_combine_kernel, dim3(T * (d.H / PFT)), dim3(PFT), 0, s, e0, e1,
