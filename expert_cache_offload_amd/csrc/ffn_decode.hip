@@ -608,6 +608,24 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
 }
 
 
+// Wait for the host's answer to this step (hybrid decode), bounded by the handle's timeout on
+// the GPU's constant 100 MHz clock; no answer in time sets ERR_HYBRID and returns false (the
+// step then goes on without the CPU experts' sum).  One thread per workgroup calls it.
+__device__ bool wait_host_answer(const Dev& v) {
+  const long long step =
+      (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+#pragma nounroll
+  while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)v.hyb_timeout_ticks) {
+      atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------- combine role
 // y[t] = bf16( sum_j sum_rs yexp[pos(t,j)][rs] + y_cpu[t] + sum_rs yexp_shared[t][rs] ), in
 // that fixed order; the routed sum skips the rows whose expert the CPU computed (hybrid
@@ -634,24 +652,7 @@ __device__ void combine_role(const FfnArgs& a, int cblk) {
     const int pos = v.inv_pos[t * d.K + j];
     s_row[i] = ncpu > 0 && v.row_cpu[pos] ? -1 : pos * RS + r;
   }
-  if (ncpu > 0 && threadIdx.x == 0) {
-    // wait for the host's answer to this step, bounded by the handle's timeout on the GPU's
-    // constant 100 MHz clock (no answer in time: ERR_HYBRID, and the step goes on without it)
-    const long long step =
-        (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
-    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-    bool ok = true;
-#pragma nounroll
-    while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step) {
-      if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)v.hyb_timeout_ticks) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-    s_ok = ok;
-    if (!ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
-  }
+  if (ncpu > 0 && threadIdx.x == 0) s_ok = wait_host_answer(v);
   __syncthreads();
   if (c >= d.H) return;
   constexpr int CH = 32;
@@ -809,23 +810,7 @@ __device__ void combine_fused_role(const FfnArgs& a, int cblk) {
     const int pos = v.inv_pos[t * d.K + j];
     s_row[i] = ncpu > 0 && v.row_cpu[pos] ? -1 : pos * RSF + r;
   }
-  if (ncpu > 0 && threadIdx.x == 0) {
-    // the host's answer to this step, bounded as in the two-kernel combine
-    const long long step =
-        (long long)(unsigned)v.hdr[HDR_STEP_LO] | ((long long)v.hdr[HDR_STEP_HI] << 32);
-    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-    bool ok = true;
-#pragma nounroll
-    while (__hip_atomic_load(&v.mail->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != step) {
-      if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)v.hyb_timeout_ticks) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-    s_ok = ok;
-    if (!ok) atomicOr(&v.ctrl[CTRL_ERR], ERR_HYBRID);
-  }
+  if (ncpu > 0 && threadIdx.x == 0) s_ok = wait_host_answer(v);
   __syncthreads();
   const int cq = threadIdx.x % (CFC / 4), pl = threadIdx.x / (CFC / 4);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
