@@ -8,6 +8,7 @@ step of the method; every replay is checked against the float64 oracle exactly a
 is: integer results bit-exact, routing weights within 1e-6, outputs within the format's
 relative-L2 tolerance.  Eager host work (copies, plan and state read-back, synchronisation)
 runs between the replays."""
+import dataclasses
 import sys
 
 import numpy as np
@@ -29,7 +30,8 @@ def _setup(wl, groups, hybrid=None):
     from expert_cache_offload_amd.runner import Workbench
     from oracle.step import Oracle
     wb = Workbench(wl, groups=groups)
-    orc = Oracle(wl, wb.pool, wb.router_np, split=hybrid)
+    shared = (lambda l: wb.shared_np[l]) if wl.has_shared else None
+    orc = Oracle(wl, wb.pool, wb.router_np, shared, split=hybrid)
     if hybrid:
         wb.set_hybrid(hybrid[0], hybrid[1], 6)
     x_static = torch.zeros((wl.layers, wb.T, wl.hidden), dtype=torch.int16, device=wb.dev)
@@ -135,3 +137,31 @@ def test_graph_whole_token(groups):
     finally:
         wb.close()
     _log(f"whole-token graph groups={groups}: max rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("groups", [0, 3])
+def test_graph_prefill_tiny(groups):
+    """Steps of many tokens (tiled router, plan, scatter, matrix-core FFN, shared expert)
+    captured one graph per layer: the 100-token chunk replayed twice through 3 layers of 24
+    slots (cold, then warm), every replay against the oracle."""
+    base = dataclasses.replace(mi.WORKLOADS["tiny"], layers=3, fixed_capacity=24, has_shared=True)
+    wl = base.as_prefill(100)
+    _log(f"case {wl.name} prefill graph per layer step, groups={groups}")
+    torch, wb, orc, x_static = _setup(wl, groups)
+    try:
+        graphs = [_capture(torch, wb, x_static, [l]) for l in range(wl.layers)]
+        with torch.cuda.stream(wb.compute):
+            x_static.copy_(wb.acts)
+        worst = 0.0
+        for c in range(2):
+            for l in range(wl.layers):
+                with torch.cuda.stream(wb.compute):
+                    graphs[l].replay()
+                wb.sync()
+                ref = orc.layer_step(c, l, wb.acts_np[l], True)
+                err = compare_step(wb, ref, f"prefill graph groups={groups} c={c} l={l}")
+                worst = max(worst, err or 0.0)
+        assert wb.stats()["steps"] == 2 * wl.layers
+    finally:
+        wb.close()
+    _log(f"prefill graph groups={groups}: max rel-L2 {worst:.2e}")
