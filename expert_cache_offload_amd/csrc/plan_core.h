@@ -221,10 +221,15 @@ __device__ inline int plan_dedup(const Dims& d, const PlanOut& o, PlanLds& s, Pl
 // in ascending expert id are computed by the CPU: no slot, no eviction, no stamp; the
 // header's miss count is then the filled misses only.  Returns false (after recording the
 // error and an empty plan) when fewer slots can be evicted than there are misses to fill.
+struct NoSplitPost {
+  __device__ void operator()(int, int) const {}
+};
+
+template <class SplitPost = NoSplitPost>
 __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o, int layer,
                                   int T, int nU, PlanLds& s, const PlanState& ps, PlanTmp& pt,
                                   const int* prot = nullptr, int n_prot = 0, int split_bc = 0,
-                                  int split_bp = 0) {
+                                  int split_bp = 0, SplitPost split_post = SplitPost{}) {
   const int E = d.E, umax = d.umax;
   for (int u = threadIdx.x; u < nU; u += RT) {
     const int sl = s.srow[s.U[u]];
@@ -248,6 +253,9 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
       pt.tmp);
   const int nCpu = miss_split(nAllMiss, split_bc, split_bp);
   const int nMiss = nAllMiss - nCpu;  // misses filled into slots: the first nMiss of the list
+  // the CPU misses are known here (the last nCpu of the list): the caller may hand them to the
+  // host before the victims are chosen (all threads call it; s.miss, s.U and s.off are synced)
+  split_post(nMiss, nCpu);
 
   // LRU victims: the `need` smallest (stamp, key) among occupied slots not used this step,
   // found in rounds of "oldest remaining stamp" (one round per distinct stamp taken: a

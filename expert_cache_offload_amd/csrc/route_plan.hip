@@ -209,12 +209,13 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
     s_rt[pos] = i / K;
     s_rw[pos] = s_tk_w[i];
   }
-  plan_cache(d, v, o, layer, T, nU, s, ps, pt, nullptr, 0, a.split_bc, a.split_bp);
-  if (a.split_bc > 0) {
-    // hybrid decode: flag the rows of the CPU experts (the combine skips them) and post the
-    // request to the host: CPU experts, the step's rows, the activations, then the step value
+  // hybrid decode: as soon as the split is known (before the victims are chosen), flag the
+  // rows of the CPU experts (the combine skips them) and post the request to the host: CPU
+  // experts, the step's rows, the activations, then the step value.  Posting ahead of the
+  // victim search and the slot-table update lets the host start that much earlier.
+  auto post = [&](int nfill, int q) {
+    if (a.split_bc <= 0) return;
     __syncthreads();
-    const int q = pt.ncpu, nfill = pt.nfill;
     for (int r = threadIdx.x; r < A; r += RT) v.row_cpu[r] = 0;
     __syncthreads();
     for (int j = threadIdx.x; j < q; j += RT) {
@@ -246,7 +247,9 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
       if (lane == 0)
         __hip_atomic_store(&m->req, ps.step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-  }
+    __syncthreads();
+  };
+  plan_cache(d, v, o, layer, T, nU, s, ps, pt, nullptr, 0, a.split_bc, a.split_bp, post);
   if (threadIdx.x == 0)
     __hip_atomic_store(&v.ctrl[CTRL_TICKET], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
