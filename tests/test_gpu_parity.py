@@ -196,11 +196,12 @@ def test_resize_into_new_arena_keeps_contents():
 
 
 def test_full_size_bf16_decode_sampled():
-    """The 48-layer 35B-A3B shape at full size (58 GB pinned pool, 1,843 slots): every integer
-    result for the first 96 token steps (4,608 layer steps), outputs sampled."""
+    """The 48-layer 35B-A3B shape at full size (58 GB pinned pool, 1,843 slots), in the launch
+    configuration the bench times (one queue): every integer result for the first 96 token
+    steps (4,608 layer steps), outputs sampled."""
     wl = mi.WORKLOADS["qwen35b_decode"].with_steps(96)
-    _log(f"case {wl.name} full size, 96 tokens")
-    with _bench(wl) as wb:
+    _log(f"case {wl.name} full size, 96 tokens, one queue")
+    with _bench(wl, groups=0) as wb:
         errs = run_parity(wb, wl.token_steps, ffn_every=97, state_every=53)
         st = wb.stats()
     _log(f"full-size: max rel-L2 {max(errs):.2e}; miss rate {st['misses'] / (st['hits'] + st['misses']):.3f}")
@@ -208,11 +209,12 @@ def test_full_size_bf16_decode_sampled():
 
 def test_full_size_fp8_decode_sampled():
     """The 284B-like fp8 shape at full width (256 experts + shared, H 4096, I 2048, 24.75 MiB
-    blobs) over 9 layers (the most a pinned host pool of this box holds), cache 17%: every
-    integer result of 48 token steps, outputs of every 47th layer step, sampled slot bytes."""
+    blobs) over 9 layers (the most a pinned host pool of this box holds), cache 17%, one queue
+    as the bench runs it: every integer result of 48 token steps, outputs of every 47th layer
+    step, sampled slot bytes."""
     wl = mi.WORKLOADS["dsv4_fp8_decode"].with_layers(9).with_steps(48)
-    _log(f"case {wl.name} full width, 48 tokens, C={wl.capacity}")
-    with _bench(wl) as wb:
+    _log(f"case {wl.name} full width, 48 tokens, C={wl.capacity}, one queue")
+    with _bench(wl, groups=0) as wb:
         errs = run_parity(wb, wl.token_steps, ffn_every=47, state_every=31)
         orc_blob = _oracle(wb).blob
         key_of = wb.snapshot()[0]
@@ -224,10 +226,11 @@ def test_full_size_fp8_decode_sampled():
 
 def test_full_size_mxfp4_four_streams_with_resize():
     """The 753B-like MXFP4 shape at full size (8 layers, 256 experts, H 6144, 41 GB pool), 4
-    streams per step for 1,024 steps with the 40% -> 15% resize before step 512: every
-    integer result of every layer step, outputs sampled on both sides of the resize."""
+    streams per step for 1,024 steps with the 40% -> 15% resize before step 512, one queue as
+    the bench runs it: every integer result of every layer step, outputs sampled on both sides
+    of the resize."""
     wl = mi.WORKLOADS["glm_mxfp4_4stream"]
     _log(f"case {wl.name} full size, {wl.token_steps} steps, C={wl.capacity}->{wl.resize_capacity}")
-    with _bench(wl) as wb:
+    with _bench(wl, groups=0) as wb:
         errs = run_parity(wb, wl.token_steps, ffn_every=2731, state_every=257)
     _log(f"full-size mxfp4: max rel-L2 {max(errs):.2e}")

@@ -155,21 +155,33 @@ def test_prefill_separate_calls_match_layer_step():
 
 
 def test_full_size_prefill_chunk_sampled():
-    """16,384-token chunk at the 35B-A3B shape over 12 layers (cache 30% = 460 slots): every
-    integer result of every layer; outputs of 4 sampled tokens on three layers."""
+    """16,384-token chunk at the 35B-A3B shape over 12 layers (cache 30% = 460 slots) in the
+    configuration the bench times (the layer's own fills in stream order, prefetch of the next
+    layer on the fill stream): every integer result of every layer step, the cache state after
+    every third step and its prefetch; outputs of 4 sampled tokens on three layers."""
     from oracle.ffn import moe_output
     from oracle.formats import bf16_to_f64, decode_blob
     wl = mi.WORKLOADS["qwen35b_prefill"].with_layers(12)
-    _log(f"case {wl.name} full chunk, C={wl.capacity}")
+    _log(f"case {wl.name} full chunk, C={wl.capacity}, prefetch, one queue for own fills")
     rng = np.random.default_rng(7)
     sample = np.sort(rng.choice(wl.tokens_per_step, 4, replace=False))
-    with _bench(wl, groups=8) as wb:
+    with _bench(wl, groups=0) as wb:
+        wb.set_prefetch(True)
         orc = _oracle(wb)
         worst = 0.0
         for l in range(wl.layers):
             wb.step(0, l)
             ref = orc.layer_step(0, l, wb.acts_np[l], False)
-            compare_step(wb, ref, f"{wl.name} l={l}", check_state=(l % 3 == 2))
+            compare_step(wb, ref, f"{wl.name} l={l}", check_state=False)
+            if l > 0:
+                assert not ref.rec.misses, "the prefetched layer should route to hits only"
+            if l + 1 < wl.layers:
+                orc.prefetch(l + 1, l, ref.U)
+            if l % 3 == 2:
+                key_of, stamp, slot_of, n, step, cap = wb.snapshot()
+                assert n == orc.cache.n and step == orc.s, (l, n, orc.cache.n, step, orc.s)
+                assert list(key_of) == orc.cache.key_of, l
+                assert list(stamp) == orc.cache.stamp, l
             if l in (0, 5, 11):
                 x = bf16_to_f64(wb.acts_np[l][sample]).reshape(len(sample), wl.hidden)
                 cache = {}
