@@ -81,6 +81,7 @@ Dims make_dims(const moe_shape& s, int max_capacity) {
   d.max_tokens = s.max_tokens;
   d.amax = s.max_tokens * s.top_k;
   d.umax = d.amax < s.experts ? d.amax : s.experts;
+  d.pw = s.max_tokens > kDecodeMaxTokens ? s.experts : d.umax;
   d.tdec = s.max_tokens < kDecodeMaxTokens ? s.max_tokens : kDecodeMaxTokens;
   d.adec = d.tdec * s.top_k;
   d.nblk = s.max_tokens > kDecodeMaxTokens ? (s.max_tokens + 63) / 64 : 0;
@@ -214,6 +215,9 @@ bool shape_ok(const moe_shape* s) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Smallest capacity of a prefetching handle: a step's distinct keys plus a whole layer.
+int prefetch_capacity_floor(const Dims& d) { return d.umax + d.E; }
 
 }  // namespace
 
@@ -546,7 +550,7 @@ moe_status moe_cache_resize(moe_cache c, int32_t new_capacity, void* new_arena, 
   if (!c) return MOE_E_INVALID;
   if (c->state != State::Idle) return MOE_E_BUSY;
   if (c->pf_layer[0] >= 0 || c->pf_layer[1] >= 0) return MOE_E_BUSY;  // prefetch in flight
-  const int floor_c = c->d.umax;
+  const int floor_c = c->prefetch ? prefetch_capacity_floor(c->d) : c->d.umax;
   if (new_capacity < floor_c || new_capacity > c->max_capacity) return MOE_E_CAPACITY;
   if (new_arena && !aligned16(new_arena)) return MOE_E_INVALID;
   if (!new_arena && new_capacity > c->arena_slots) return MOE_E_CAPACITY;
@@ -638,6 +642,9 @@ moe_status moe_set_prefetch(moe_cache c, int32_t enable) {
   if (!c || (enable != 0 && enable != 1)) return MOE_E_INVALID;
   if (enable && c->d.nblk == 0) return MOE_E_INVALID;  // a handle for decode steps only
   if (c->state != State::Idle || c->pf_layer[0] >= 0 || c->pf_layer[1] >= 0) return MOE_E_BUSY;
+  // a prefetch keeps the step's distinct keys (up to umax) and brings every expert of the
+  // next layer: the cache must hold both, or the plan would run out of evictable slots
+  if (enable && c->capacity < prefetch_capacity_floor(c->d)) return MOE_E_CAPACITY;
   c->prefetch = enable;
   return MOE_OK;
 }

@@ -73,6 +73,8 @@ constexpr int kMaxTokens = 65536;    // most tokens of one layer step
 struct Dims {
   int L, E, K, H, I, fmt, has_shared, max_tokens;
   int umax;          // min(max_tokens*K, E): distinct experts per step
+  int pw;            // entries of the plan's per-expert LDS arrays: umax, or E when the
+                     // handle has the many-token path (a prefetch plans all E experts)
   int amax;          // max_tokens*K: (token, choice) assignments per step
   int tdec;          // min(max_tokens, kDecodeMaxTokens): tokens of the decode path
   int adec;          // tdec*K
@@ -195,10 +197,15 @@ constexpr int kMaxFillGroups = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
+// fp32 -> bf16, round to nearest even.  A NaN stays a NaN of the same sign (quieted): the
+// rounding bias must not carry its payload into the exponent or the sign.
+__host__ __device__ __forceinline__ uint16_t bf16_bits_rne(uint32_t u) {
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  return bf16_bits_rne(__float_as_uint(f));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

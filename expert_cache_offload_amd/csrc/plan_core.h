@@ -59,45 +59,47 @@ struct PlanLds {
   int* cnt;        // [E] assignments per expert this step
   int* uidx;       // [E] position of an expert in U, -1 if unused
   int* srow;       // [E] this layer's row of slot_of
-  int* U;          // [umax] + the arrays below, per position in U unless noted
-  int* off;        // [umax + 1]
+  int* U;          // [pw] + the arrays below, per position in U unless noted
+  int* off;        // [pw + 1]
   int* uslot;
   int* hit;
-  int* miss;       // [umax] miss list (positions in U)
-  int* vict;       // [umax] victim slots in eviction order
-  int* vkey;       // [umax] their keys
+  int* miss;       // [pw] miss list (positions in U)
+  int* vict;       // [pw] victim slots in eviction order
+  int* vkey;       // [pw] their keys
   int* grp;
   int* sorted;
-  int* aslot;      // [umax] per miss: assigned slot
-  int* avkey;      // [umax] per miss: evicted key or -1
-  int* hitl;       // [umax] hit list (positions in U)
+  int* aslot;      // [pw] per miss: assigned slot
+  int* avkey;      // [pw] per miss: evicted key or -1
+  int* hitl;       // [pw] hit list (positions in U)
 };
 
+// The arrays indexed by a position in U (and the victim group buffers) hold d.pw entries:
+// the step's distinct experts (at most umax), or every expert of a layer for a prefetch plan.
 inline __host__ __device__ size_t plan_lds_bytes(const Dims& d) {
   size_t b = sizeof(uint64_t) * (size_t)d.max_capacity;
   b += sizeof(int) * 3 * (size_t)d.E;
-  b += sizeof(int) * (size_t)(12 * d.umax + 1);
+  b += sizeof(int) * (size_t)(12 * d.pw + 1);
   return (b + 15) & ~(size_t)15;
 }
 
 __device__ inline unsigned char* plan_carve(const Dims& d, unsigned char* p, PlanLds& s) {
-  const int umax = d.umax;
+  const int pw = d.pw;
   s.comp = (uint64_t*)p;  p += sizeof(uint64_t) * d.max_capacity;
   s.cnt = (int*)p;        p += sizeof(int) * d.E;
   s.uidx = (int*)p;       p += sizeof(int) * d.E;
   s.srow = (int*)p;       p += sizeof(int) * d.E;
-  s.U = (int*)p;          p += sizeof(int) * umax;
-  s.off = (int*)p;        p += sizeof(int) * (umax + 1);
-  s.uslot = (int*)p;      p += sizeof(int) * umax;
-  s.hit = (int*)p;        p += sizeof(int) * umax;
-  s.miss = (int*)p;       p += sizeof(int) * umax;
-  s.vict = (int*)p;       p += sizeof(int) * umax;
-  s.vkey = (int*)p;       p += sizeof(int) * umax;
-  s.grp = (int*)p;        p += sizeof(int) * umax;
-  s.sorted = (int*)p;     p += sizeof(int) * umax;
-  s.aslot = (int*)p;      p += sizeof(int) * umax;
-  s.avkey = (int*)p;      p += sizeof(int) * umax;
-  s.hitl = (int*)p;       p += sizeof(int) * umax;
+  s.U = (int*)p;          p += sizeof(int) * pw;
+  s.off = (int*)p;        p += sizeof(int) * (pw + 1);
+  s.uslot = (int*)p;      p += sizeof(int) * pw;
+  s.hit = (int*)p;        p += sizeof(int) * pw;
+  s.miss = (int*)p;       p += sizeof(int) * pw;
+  s.vict = (int*)p;       p += sizeof(int) * pw;
+  s.vkey = (int*)p;       p += sizeof(int) * pw;
+  s.grp = (int*)p;        p += sizeof(int) * pw;
+  s.sorted = (int*)p;     p += sizeof(int) * pw;
+  s.aslot = (int*)p;      p += sizeof(int) * pw;
+  s.avkey = (int*)p;      p += sizeof(int) * pw;
+  s.hitl = (int*)p;       p += sizeof(int) * pw;
   // align by adding an offset: a round trip through an integer would lose the pointer's
   // LDS address space, and every access through it would become a flat access
   return p + ((16 - ((uintptr_t)p & 15)) & 15);
@@ -230,7 +232,7 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
                                   int T, int nU, PlanLds& s, const PlanState& ps, PlanTmp& pt,
                                   const int* prot = nullptr, int n_prot = 0, int split_bc = 0,
                                   int split_bp = 0, SplitPost split_post = SplitPost{}) {
-  const int E = d.E, umax = d.umax;
+  const int E = d.E, pw = d.pw;
   for (int u = threadIdx.x; u < nU; u += RT) {
     const int sl = s.srow[s.U[u]];
     s.uslot[u] = sl;
@@ -259,7 +261,8 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
 
   // LRU victims: the `need` smallest (stamp, key) among occupied slots not used this step,
   // found in rounds of "oldest remaining stamp" (one round per distinct stamp taken: a
-  // step stamps all of its experts alike, so a group never exceeds umax)
+  // step stamps all of its experts alike, so a group never exceeds pw - at most umax keys
+  // for a routed step, E for a prefetch step)
   const int n = ps.n, C = ps.C;
   const int nfree = C - n;
   const int need = nMiss > nfree ? nMiss - nfree : 0;
@@ -295,11 +298,11 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
         const uint64_t c = s.comp[i];
         if (c != NONE && (uint32_t)(c >> 32) == st) {
           const int q = atomicAdd(&pt.g, 1);
-          if (q < umax) s.grp[q] = i;
+          if (q < pw) s.grp[q] = i;
         }
       }
       __syncthreads();
-      const int g = pt.g < umax ? pt.g : umax;
+      const int g = pt.g < pw ? pt.g : pw;
       for (int q = threadIdx.x; q < g; q += RT) {  // order the group by key
         const uint32_t kq = (uint32_t)s.comp[s.grp[q]];
         int rank = 0;

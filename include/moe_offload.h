@@ -171,7 +171,8 @@ moe_status moe_cache_destroy(moe_cache cache);
  * every surviving slot and becomes the arena, after which the old arena may be
  * released once `stream` has passed this call.  Stream ordered.
  * MOE_E_BUSY if a step is in flight, MOE_E_CAPACITY outside
- * [min(max_tokens*top_k, experts), max_capacity]. */
+ * [min(max_tokens*top_k, experts), max_capacity] (with prefetch on, the lower end is
+ * min(max_tokens*top_k, experts) + experts; see moe_set_prefetch). */
 moe_status moe_cache_resize(moe_cache cache, int32_t new_capacity, void* new_arena, void* stream);
 
 /* Router GEMM + top-k + dedup + classification + LRU victims + slot-table update
@@ -228,7 +229,10 @@ moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int32_t* stamp,
  * them.  The caller's next layer step must then be layer l + 1.  Decode steps (T <= 8) never
  * prefetch.  enable: 0 or 1.  MOE_E_INVALID for a handle with max_tokens <= 8; MOE_E_BUSY
  * while a step or a prefetch is in flight (moe_cache_resize is MOE_E_BUSY too until the
- * prefetched layer's step has run). */
+ * prefetched layer's step has run); MOE_E_CAPACITY when enabling on a cache of fewer than
+ * min(max_tokens*top_k, experts) + experts slots (the step's distinct experts stay protected
+ * while every expert of the next layer comes in), and while prefetch is on moe_cache_resize
+ * refuses to shrink below that floor. */
 moe_status moe_set_prefetch(moe_cache cache, int32_t enable);
 
 /* Hybrid decode: split each decode step's misses between PCIe fills and in-place CPU

@@ -95,6 +95,45 @@ def test_prefill_prefetch_qwen_shape():
     _log(f"qwen prefetch: max rel-L2 {max(errs):.2e}, misses {st['misses']}")
 
 
+@pytest.mark.parametrize("k,hidden,inter,cap", [(8, 2048, 768, 260), (2, 256, 128, 160)])
+def test_prefetch_steps_smaller_than_a_layer(k, hidden, inter, cap):
+    """Prefetch on handles whose steps hold fewer distinct experts than a layer has (128
+    experts, max_tokens 9: at most 9*k distinct per step, while a prefetch plans all 128), 6
+    layers.  With top-2 a prefetch group of ~110 keys stamped alike outlives its step and is
+    evicted by the next prefetch; every step, and the state after each prefetch, against R8."""
+    wl = mi.Workload(f"e128_k{k}_h{hidden}_prefill9", 6, hidden, 128, k, inter, 0, 0.0, 9, 1,
+                     "prefill", fixed_capacity=cap)
+    _log(f"case {wl.name} prefetch C={cap}")
+    with _bench(wl, groups=0) as wb:
+        errs = _run_chunk_prefetch(wb)
+        st = wb.stats()
+    _log(f"{wl.name}: max rel-L2 {max(errs):.2e}, misses {st['misses']}")
+
+
+def test_prefetch_capacity_floor_refused():
+    """Prefetch needs min(max_tokens*k, E) + E slots (the step's protected keys plus a whole
+    layer): refused on the host below that, and a resize below it is refused while prefetch
+    is on (no kernel runs for a refused call)."""
+    from expert_cache_offload_amd import MOE_E_CAPACITY, MoeError
+    wl = mi.Workload("e128_k8_prefill9_floor", 2, 256, 128, 8, 128, 0, 0.0, 9, 1, "prefill",
+                     fixed_capacity=199)
+    _log(f"case {wl.name}")
+    with _bench(wl, groups=0, max_capacity=260) as wb:
+        with pytest.raises(MoeError) as ei:
+            wb.set_prefetch(True)
+        assert ei.value.status == MOE_E_CAPACITY
+        wb.prefetch = False
+        wb.resize(200)
+        wb.set_prefetch(True)
+        with pytest.raises(MoeError) as ei:
+            wb.resize(199)
+        assert ei.value.status == MOE_E_CAPACITY
+        wb.set_prefetch(False)
+        wb.resize(199)
+        key_of, stamp, slot_of, n, step, cap = wb.snapshot()
+        assert cap == 199 and n == 0 and step == 0
+
+
 def test_prefill_tiny_shape_with_shared_expert():
     """16 experts top-2 at hidden 256: 100 tokens (one full and one ragged 64-token block,
     row tiles far from full), three layers over 24 slots so the later layers evict."""
