@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_OFFLOAD_LIB") or os.path.join(_HERE, "libmoe_offload.so")
 
 MOE_OK, MOE_E_INVALID, MOE_E_CAPACITY, MOE_E_BUSY, MOE_E_HIP, MOE_E_NOMEM = 0, -1, -2, -3, -4, -5
-MOE_E_HYBRID = -6
+MOE_E_HYBRID, MOE_E_SCRATCH = -6, -7
 MOE_FMT_BF16, MOE_FMT_FP8_E4M3_K128, MOE_FMT_MXFP4_K32 = 0, 1, 2
 
 # PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7).  Loading torch
@@ -77,6 +77,8 @@ _SIGS = {
     "moe_host_pool_free": (_i32, [_vp]),
     "moe_cache_create": (_i32, [ctypes.POINTER(MoeShape), _i32, _i32, _vp, _vp, _vp, _vp,
                                 ctypes.POINTER(_vp)]),
+    "moe_cache_create_static": (_i32, [ctypes.POINTER(MoeShape), _i32, _i32, _vp, _vp, _vp,
+                                       ctypes.POINTER(_vp)]),
     "moe_cache_destroy": (_i32, [_vp]),
     "moe_cache_resize": (_i32, [_vp, _i32, _vp, _vp]),
     "moe_route_classify": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
@@ -162,6 +164,16 @@ def moe_cache_create(shape: MoeShape, capacity: int, max_capacity: int, slot_are
     st = _lib.moe_cache_create(ctypes.byref(shape), capacity, max_capacity, _p(slot_arena),
                                _p(workspace), _p(host_pool), stream, ctypes.byref(out))
     _check(st, "moe_cache_create")
+    return int(out.value)
+
+
+def moe_cache_create_static(shape: MoeShape, capacity: int, max_capacity: int, slot_arena,
+                            host_pool, stream: int = 0) -> int:
+    """moe_cache_create with the library's static per-device workspace (no allocation)."""
+    out = _vp()
+    st = _lib.moe_cache_create_static(ctypes.byref(shape), capacity, max_capacity,
+                                      _p(slot_arena), _p(host_pool), stream, ctypes.byref(out))
+    _check(st, "moe_cache_create_static")
     return int(out.value)
 
 

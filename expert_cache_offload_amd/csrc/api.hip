@@ -7,6 +7,7 @@
 #include <chrono>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <thread>
 #include <vector>
@@ -378,6 +379,8 @@ struct moe_cache_s {
   void* workspace;
   const void* host_pool;
   const void* pool_dev;
+  int static_dev = -1;  // device whose static workspace this handle holds, or -1
+  bool events = false;  // the events below exist (created on first multi-queue use)
   hipEvent_t ev_plan;
   hipEvent_t ev_fill[kMaxGroups];
   int prefetch;                    // prefetch the next layer in steps of many tokens
@@ -390,6 +393,45 @@ struct moe_cache_s {
   int fill_groups;
   int last_hip;
 };
+
+// The library's own workspace, for callers that cannot allocate device memory
+// (moe_cache_create_static): one array per device, taken by at most one live handle at a
+// time.  Host code never uses the array's name as an address: each device's address comes
+// from hipGetSymbolAddress, asked once per device with that device current.
+constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_static_mu;
+static void* g_static_ptr[kMaxDevices];  // device address of `scratch` on each device
+static bool g_static_busy[kMaxDevices];  // a live handle holds that device's array
+
+static moe_status static_workspace_acquire(int* dev_out, void** ptr_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MOE_E_HIP;
+  }
+  std::lock_guard<std::mutex> g(g_static_mu);
+  if (g_static_busy[dev]) return MOE_E_BUSY;
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_E_HIP;
+    }
+    g_static_ptr[dev] = p;
+  }
+  g_static_busy[dev] = true;
+  *dev_out = dev;
+  *ptr_out = g_static_ptr[dev];
+  return MOE_OK;
+}
+
+static void static_workspace_release(int dev) {
+  std::lock_guard<std::mutex> g(g_static_mu);
+  g_static_busy[dev] = false;
+}
 
 static moe_status hip_fail(moe_cache c, hipError_t e) {
   if (c) c->last_hip = (int)e;
@@ -470,9 +512,23 @@ moe_status moe_host_pool_free(void* p) {
   return hipHostFree(p) == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
-moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t max_capacity,
-                            void* slot_arena, void* workspace, const void* host_pool,
-                            void* stream, moe_cache* out) {
+// Events joining the compute and fill queues (and the prefetch); created on first use, so a
+// handle driven on one queue (moe_layer_step with groups == 0, no prefetch) creates none.
+static hipError_t ensure_events(moe_cache c) {
+  if (c->events) return hipSuccess;
+  hipError_t e = hipEventCreateWithFlags(&c->ev_plan, hipEventDisableTiming);
+  for (int g = 0; g < kMaxGroups && e == hipSuccess; ++g)
+    e = hipEventCreateWithFlags(&c->ev_fill[g], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_pfplan, hipEventDisableTiming);
+  for (int q = 0; q < 2 && e == hipSuccess; ++q)
+    e = hipEventCreateWithFlags(&c->ev_pf[q], hipEventDisableTiming);
+  c->events = true;  // (partially) created: destroy releases whatever exists
+  return e;
+}
+
+static moe_status create_impl(const moe_shape* shape, int32_t capacity, int32_t max_capacity,
+                              void* slot_arena, void* workspace, const void* host_pool,
+                              void* stream, moe_cache* out) {
   if (!out) return MOE_E_INVALID;
   *out = nullptr;
   if (!shape_ok(shape) || !slot_arena || !workspace || !host_pool) return MOE_E_INVALID;
@@ -502,20 +558,41 @@ moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t ma
   c->host_pool = host_pool;
   c->pool_dev = pool_dev;
   c->state = State::Idle;
-  hipError_t e = hipEventCreateWithFlags(&c->ev_plan, hipEventDisableTiming);
-  for (int g = 0; g < kMaxGroups && e == hipSuccess; ++g)
-    e = hipEventCreateWithFlags(&c->ev_fill[g], hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_pfplan, hipEventDisableTiming);
-  for (int q = 0; q < 2 && e == hipSuccess; ++q)
-    e = hipEventCreateWithFlags(&c->ev_pf[q], hipEventDisableTiming);
-  if (e == hipSuccess)
-    e = launch_init(c->v, max_capacity, shape->layers * shape->experts, capacity,
-                    (hipStream_t)stream);
+  hipError_t e = launch_init(c->v, max_capacity, shape->layers * shape->experts, capacity,
+                             (hipStream_t)stream);
   if (e != hipSuccess) {
     moe_cache_destroy(c);
     return MOE_E_HIP;
   }
   *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t max_capacity,
+                            void* slot_arena, void* workspace, const void* host_pool,
+                            void* stream, moe_cache* out) {
+  return create_impl(shape, capacity, max_capacity, slot_arena, workspace, host_pool, stream,
+                     out);
+}
+
+moe_status moe_cache_create_static(const moe_shape* shape, int32_t capacity,
+                                   int32_t max_capacity, void* slot_arena,
+                                   const void* host_pool, void* stream, moe_cache* out) {
+  if (!out) return MOE_E_INVALID;
+  *out = nullptr;
+  if (!shape_ok(shape)) return MOE_E_INVALID;
+  if (max_capacity < 1 || max_capacity > kMaxCapacity) return MOE_E_CAPACITY;
+  if (moe_workspace_bytes(shape, max_capacity) > kStaticWorkspaceBytes) return MOE_E_SCRATCH;
+  int dev = -1;
+  void* ws = nullptr;
+  moe_status st = static_workspace_acquire(&dev, &ws);
+  if (st != MOE_OK) return st;
+  st = create_impl(shape, capacity, max_capacity, slot_arena, ws, host_pool, stream, out);
+  if (st != MOE_OK) {
+    static_workspace_release(dev);
+    return st;
+  }
+  (*out)->static_dev = dev;
   return MOE_OK;
 }
 
@@ -536,12 +613,15 @@ moe_status moe_cache_destroy(moe_cache c) {
   hybrid_stop(c);
   (void)c->prof.harvest_all();
   c->prof.destroy();
-  if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
-  for (int g = 0; g < kMaxGroups; ++g)
-    if (c->ev_fill[g]) (void)hipEventDestroy(c->ev_fill[g]);
-  if (c->ev_pfplan) (void)hipEventDestroy(c->ev_pfplan);
-  for (int q = 0; q < 2; ++q)
-    if (c->ev_pf[q]) (void)hipEventDestroy(c->ev_pf[q]);
+  if (c->events) {
+    if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
+    for (int g = 0; g < kMaxGroups; ++g)
+      if (c->ev_fill[g]) (void)hipEventDestroy(c->ev_fill[g]);
+    if (c->ev_pfplan) (void)hipEventDestroy(c->ev_pfplan);
+    for (int q = 0; q < 2; ++q)
+      if (c->ev_pf[q]) (void)hipEventDestroy(c->ev_pf[q]);
+  }
+  if (c->static_dev >= 0) static_workspace_release(c->static_dev);
   delete c;
   return MOE_OK;
 }
@@ -613,7 +693,8 @@ static hipError_t ffn_launch(moe_cache c, const void* x, int T, const void* shar
 // right after the step plan before it, its fills on `fs` (after the fills already queued
 // there); the FFN of `layer` waits for them.
 static hipError_t issue_prefetch(moe_cache c, int layer, hipStream_t cs, hipStream_t fs) {
-  hipError_t e = launch_prefetch_plan(c->d, c->v, layer, cs);
+  hipError_t e = ensure_events(c);
+  if (e == hipSuccess) e = launch_prefetch_plan(c->d, c->v, layer, cs);
   if (e == hipSuccess && fs != cs) {
     e = hipEventRecord(c->ev_pfplan, cs);
     if (e == hipSuccess) e = hipStreamWaitEvent(fs, c->ev_pfplan, 0);
@@ -769,7 +850,8 @@ moe_status moe_route_classify(moe_cache c, int32_t layer, const void* x, int32_t
   if (T > 0 && (!x || !w_router || !aligned16(x) || !aligned16(w_router))) return MOE_E_INVALID;
   if (T > kDecodeMaxTokens && !many_tokens_ok(c->d)) return MOE_E_INVALID;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = route_launch(c, layer, x, T, w_router, topk_idx, topk_w, s);
+  hipError_t e = ensure_events(c);
+  if (e == hipSuccess) e = route_launch(c, layer, x, T, w_router, topk_idx, topk_w, s);
   if (e == hipSuccess) e = hipEventRecord(c->ev_plan, s);
   if (e != hipSuccess) return hip_fail(c, e);
   c->state = State::Planned;
@@ -997,6 +1079,8 @@ const char* moe_status_string(moe_status s) {
     case MOE_E_HIP: return "HIP runtime error";
     case MOE_E_NOMEM: return "pinned host memory unavailable";
     case MOE_E_HYBRID: return "hybrid decode: the host did not answer a step in time";
+    case MOE_E_SCRATCH:
+      return "workspace larger than the library's static workspace (16 MiB per device)";
     default: return "unknown status";
   }
 }

@@ -73,6 +73,7 @@ typedef int32_t moe_status;
 #define MOE_E_HIP (-4)      /* a HIP runtime call failed; see moe_last_hip_error */
 #define MOE_E_NOMEM (-5)    /* pinned host allocation failed */
 #define MOE_E_HYBRID (-6)   /* hybrid decode: the host did not answer a step within ~2 s */
+#define MOE_E_SCRATCH (-7)  /* workspace above the static workspace (moe_cache_create_static) */
 
 #define MOE_FMT_BF16 0
 #define MOE_FMT_FP8_E4M3_K128 1
@@ -159,6 +160,20 @@ moe_status moe_host_pool_free(void* p);
 moe_status moe_cache_create(const moe_shape* shape, int32_t capacity, int32_t max_capacity,
                             void* slot_arena, void* workspace, const void* host_pool,
                             void* stream, moe_cache* out);
+
+/* For callers that cannot allocate device memory (code under hipGraph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moe_cache_create with the workspace taken from the
+ * library's own static device array of 16 MiB per device (enough for the decode handles of
+ * every shape here; moe_workspace_bytes(shape, max_capacity) must not exceed it, else
+ * MOE_E_SCRATCH).  Allocates nothing, on the device or through any allocating library
+ * routine; the handle's state is initialised on `stream` as with moe_cache_create.  The
+ * array is shared by every call on the device and keeps the last handle's contents: at most
+ * one live handle per device may hold it (a second create while one lives returns
+ * MOE_E_BUSY; overlapping use would race); moe_cache_destroy gives it back.  Events are
+ * created only when a step first joins two queues (groups >= 1 or prefetch). */
+moe_status moe_cache_create_static(const moe_shape* shape, int32_t capacity,
+                                   int32_t max_capacity, void* slot_arena,
+                                   const void* host_pool, void* stream, moe_cache* out);
 
 moe_status moe_cache_destroy(moe_cache cache);
 
