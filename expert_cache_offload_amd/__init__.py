@@ -93,9 +93,16 @@ _SIGS = {
     "moe_set_hybrid": (_i32, [_vp, _i32, _i32, _i32]),
     "moe_auto_capacity": (_i32, [ctypes.POINTER(MoeShape), ctypes.c_uint64, ctypes.c_uint64,
                                  ctypes.c_double, ctypes.POINTER(_i32)]),
+    "moe_auto_capacity_device": (_i32, [ctypes.POINTER(MoeShape), ctypes.c_uint64,
+                                        ctypes.c_double, ctypes.POINTER(_i32),
+                                        ctypes.POINTER(ctypes.c_uint64)]),
     "moe_pool_write": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
     "moe_pool_read": (_i32, [ctypes.c_char_p, ctypes.POINTER(MoeShape), _vp, _i32]),
     "moe_miss_split": (_i32, [_i32, _i32, _i32]),
+    "moe_choose_mode": (_i32, [_i32, ctypes.c_double, ctypes.c_double]),
+    "moe_probe_stream_read": (_i32, [_vp, ctypes.c_uint64, ctypes.c_uint64, _i32, _i32, _vp,
+                                     _vp, ctypes.POINTER(ctypes.c_double)]),
+    "moe_probe_empty_launch": (_i32, [_i32, _i32, _vp, ctypes.POINTER(ctypes.c_double)]),
     "moe_set_hybrid_timeout": (_i32, [_vp, _i64]),
     "moe_hybrid_hold": (_i32, [_vp, _i32]),
     "moe_hybrid_read": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
@@ -273,6 +280,17 @@ def moe_auto_capacity(shape: MoeShape, free_bytes: int, reserve_bytes: int,
     return int(c.value)
 
 
+def moe_auto_capacity_device(shape: MoeShape, reserve_bytes: int,
+                             offload_ratio: float = -1.0) -> tuple[int, int]:
+    """(capacity, free bytes it was sized from): moe_auto_capacity over the device's free
+    memory."""
+    c, fr = _i32(0), ctypes.c_uint64(0)
+    _check(_lib.moe_auto_capacity_device(ctypes.byref(shape), int(reserve_bytes),
+                                         float(offload_ratio), ctypes.byref(c),
+                                         ctypes.byref(fr)), "moe_auto_capacity_device")
+    return int(c.value), int(fr.value)
+
+
 def moe_pool_write(path: str, shape: MoeShape, pool: int, threads: int = 8) -> None:
     _check(_lib.moe_pool_write(path.encode(), ctypes.byref(shape), pool, int(threads)),
            "moe_pool_write")
@@ -320,11 +338,36 @@ def moe_cpu_expert_rate(shape: MoeShape, pool: int, n_blobs: int, threads: int,
     return float(g.value)
 
 
-def choose_hybrid(cpu_gbps: float, offload_gbps: float, threshold: float = 2.0) -> bool:
-    """Mode choice per dtype: split misses with the CPU only when its expert rate is at
-    least `threshold` times the offload rate ("FreeToken: az VRAM ile büyük MoE modelleri",
-    "Tuzaklar": a 2.0x threshold)."""
-    return cpu_gbps > 0 and offload_gbps > 0 and cpu_gbps >= threshold * offload_gbps
+def moe_choose_mode(wfmt: int, cpu_gbps: float, fill_gbps: float) -> int:
+    """1: hybrid decode, 0: fill every miss, -1: invalid (the library's 2.0x rule)."""
+    return int(_lib.moe_choose_mode(int(wfmt), float(cpu_gbps), float(fill_gbps)))
+
+
+def choose_hybrid(cpu_gbps: float, offload_gbps: float, wfmt: int = MOE_FMT_BF16) -> bool:
+    """True when the library's mode rule picks hybrid decode for this format and these rates."""
+    r = moe_choose_mode(wfmt, cpu_gbps, offload_gbps)
+    if r < 0:
+        raise ValueError(f"moe_choose_mode: invalid rates or format ({wfmt}, {cpu_gbps}, "
+                         f"{offload_gbps})")
+    return r == 1
+
+
+def moe_probe_stream_read(buf, span_bytes: int, bytes_per_launch: int, nontemporal: bool,
+                          reps: int, sink, stream: int = 0) -> float:
+    """Average duration (us) of a streaming-read launch of bytes_per_launch (see the header)."""
+    us = ctypes.c_double(0.0)
+    _check(_lib.moe_probe_stream_read(_p(buf), int(span_bytes), int(bytes_per_launch),
+                                      int(bool(nontemporal)), int(reps), _p(sink), stream,
+                                      ctypes.byref(us)), "moe_probe_stream_read")
+    return float(us.value)
+
+
+def moe_probe_empty_launch(grid: int, reps: int, stream: int = 0) -> float:
+    """Average duration (us) of an empty launch of `grid` workgroups."""
+    us = ctypes.c_double(0.0)
+    _check(_lib.moe_probe_empty_launch(int(grid), int(reps), stream, ctypes.byref(us)),
+           "moe_probe_empty_launch")
+    return float(us.value)
 
 
 def moe_profile_enable(handle: int, mask: int = PROF_ALL, every: int = 1) -> None:

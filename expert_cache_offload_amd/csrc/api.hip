@@ -46,6 +46,9 @@ hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const 
                               int T, int stage, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 bool prefill_ffn_supported(const Dims& d);
 hipError_t launch_prefetch_plan(const Dims& d, const Dev& v, int layer, hipStream_t s);
+hipError_t probe_stream_read(const void* buf, size_t span, size_t bytes, int nt, int reps,
+                             uint32_t* sink, hipStream_t s, double* avg_us);
+hipError_t probe_empty_launch(int grid, int reps, hipStream_t s, double* avg_us);
 }  // namespace moe
 
 using namespace moe;
@@ -53,6 +56,9 @@ using namespace moe;
 namespace {
 
 constexpr int kMaxGroups = kMaxFillGroups;
+// CPU expert rate over offload rate at which a format switches to hybrid decode ("FreeToken:
+// az VRAM ile büyük MoE modelleri", "Tuzaklar": the start-up probe's 2.0x threshold).
+constexpr double kHybridThreshold = 2.0;
 constexpr int kMaxCapacity = kMaxSlots;  // LDS-resident LRU stamps and the resize sort
 // Fill workgroups: 32 saturate the PCIe link (57 GB/s measured) while leaving HBM streaming
 // of concurrent kernels untouched; 256 workgroups collapse a concurrent HBM stream to <2%.
@@ -494,6 +500,19 @@ moe_status moe_auto_capacity(const moe_shape* shape, uint64_t free_bytes, uint64
   return MOE_OK;
 }
 
+moe_status moe_auto_capacity_device(const moe_shape* shape, uint64_t reserve_bytes,
+                                    double offload_ratio, int32_t* capacity,
+                                    uint64_t* free_bytes) {
+  if (!shape_ok(shape) || !capacity) return MOE_E_INVALID;
+  size_t fr = 0, total = 0;
+  if (hipMemGetInfo(&fr, &total) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_E_HIP;
+  }
+  if (free_bytes) *free_bytes = (uint64_t)fr;
+  return moe_auto_capacity(shape, (uint64_t)fr, reserve_bytes, offload_ratio, capacity);
+}
+
 moe_status moe_host_pool_alloc(size_t bytes, void** out) {
   if (!out || bytes == 0) return MOE_E_INVALID;
   void* p = nullptr;
@@ -771,6 +790,41 @@ moe_status moe_set_hybrid(moe_cache c, int32_t b_cpu_mbps, int32_t b_pcie_mbps, 
   }
   c->split_bc = b_cpu_mbps;
   c->split_bp = b_pcie_mbps;
+  return MOE_OK;
+}
+
+int32_t moe_choose_mode(int32_t wfmt, double cpu_gbps, double fill_gbps) {
+  if (wfmt < MOE_FMT_BF16 || wfmt > MOE_FMT_MXFP4_K32) return -1;
+  if (!(cpu_gbps >= 0.0) || !(fill_gbps >= 0.0)) return -1;  // negative or NaN
+  if (wfmt != MOE_FMT_BF16) return 0;  // no CPU expert path for block-scaled formats
+  return cpu_gbps > 0.0 && fill_gbps > 0.0 && cpu_gbps >= kHybridThreshold * fill_gbps ? 1 : 0;
+}
+
+moe_status moe_probe_stream_read(const void* buf, uint64_t span_bytes, uint64_t bytes_per_launch,
+                                 int32_t nontemporal, int32_t reps, void* sink, void* stream,
+                                 double* avg_us) {
+  if (!buf || !sink || !avg_us || reps < 1 || reps > 100000) return MOE_E_INVALID;
+  if (!aligned16(buf) || ((uintptr_t)sink & 3)) return MOE_E_INVALID;
+  if (bytes_per_launch < 16 || bytes_per_launch % 16 || bytes_per_launch > span_bytes)
+    return MOE_E_INVALID;
+  if (nontemporal != 0 && nontemporal != 1) return MOE_E_INVALID;
+  const hipError_t e = probe_stream_read(buf, span_bytes, bytes_per_launch, nontemporal, reps,
+                                         (uint32_t*)sink, (hipStream_t)stream, avg_us);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_E_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_probe_empty_launch(int32_t grid, int32_t reps, void* stream, double* avg_us) {
+  if (!avg_us || grid < 1 || grid > (1 << 20) || reps < 1 || reps > 100000)
+    return MOE_E_INVALID;
+  const hipError_t e = probe_empty_launch(grid, reps, (hipStream_t)stream, avg_us);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_E_HIP;
+  }
   return MOE_OK;
 }
 

@@ -203,6 +203,13 @@ constexpr int GN = 4;  // gate chunks per lane per pass (4 * GN weight loads in 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
+// Expert weights are read once per step: streaming (non-temporal) loads, so they do not
+// displace the activations, partials and plan tables from the caches.
+template <class V>
+__device__ __forceinline__ V ld_stream(const unsigned char* p) {
+  return __builtin_nontemporal_load((const V*)p);
+}
+
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w),
                                          __builtin_bit_cast(bf16x2v, x), acc, false);
@@ -357,10 +364,10 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
     for (int k = 0; k < GN; ++k) {
       int c = (kb + k) * 64 + lane;
       c = c < ngq ? c : ngq - 1;  // in-row address; masked below
-      wg0[k] = *(const u32x4v*)(r0 + (size_t)c * 16);
-      wu0[k] = *(const u32x4v*)(r0 + hbytes + (size_t)c * 16);
-      wg1[k] = *(const u32x4v*)(r1 + (size_t)c * 16);
-      wu1[k] = *(const u32x4v*)(r1 + hbytes + (size_t)c * 16);
+      wg0[k] = ld_stream<u32x4v>(r0 + (size_t)c * 16);
+      wu0[k] = ld_stream<u32x4v>(r0 + hbytes + (size_t)c * 16);
+      wg1[k] = ld_stream<u32x4v>(r1 + (size_t)c * 16);
+      wu1[k] = ld_stream<u32x4v>(r1 + hbytes + (size_t)c * 16);
     }
     if constexpr (F::SB > 0) {
 #pragma unroll
@@ -536,7 +543,7 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
   const unsigned char* wp = wdt + (size_t)ra * drow + F::row_bytes(c0);
   W w[DMAXR];
 #pragma unroll
-  for (int r = 0; r < DMAXR; ++r) w[r] = *(const W*)(wp + (size_t)(r < nrw ? r : nrw - 1) * drow);
+  for (int r = 0; r < DMAXR; ++r) w[r] = ld_stream<W>(wp + (size_t)(r < nrw ? r : nrw - 1) * drow);
   float sc0[DC], sc1[DC];
   int bsplit = DMAXR;  // first r that uses sc1
   if constexpr (F::SB > 0) {
@@ -729,14 +736,14 @@ __device__ void fused_role(const FfnArgs& a, const Entry& en, int rb, u32x4v (&x
     for (int k = 0; k < GN; ++k) {
       int c = (kb + k) * 64 + lane;
       c = c < ngq ? c : ngq - 1;  // in-row address; masked below
-      wg0[k] = *(const u32x4v*)(r0 + (size_t)c * 16);
-      wu0[k] = *(const u32x4v*)(r0 + hbytes + (size_t)c * 16);
-      wg1[k] = *(const u32x4v*)(r1 + (size_t)c * 16);
-      wu1[k] = *(const u32x4v*)(r1 + hbytes + (size_t)c * 16);
+      wg0[k] = ld_stream<u32x4v>(r0 + (size_t)c * 16);
+      wu0[k] = ld_stream<u32x4v>(r0 + hbytes + (size_t)c * 16);
+      wg1[k] = ld_stream<u32x4v>(r1 + (size_t)c * 16);
+      wu1[k] = ld_stream<u32x4v>(r1 + hbytes + (size_t)c * 16);
     }
     if (kb == 0) {  // the WdT rows go out behind the first pass, before any product
 #pragma unroll
-      for (int r = 0; r < NR; ++r) wd[r] = *(const u32x4v*)(wdt + (size_t)r * hbytes);
+      for (int r = 0; r < NR; ++r) wd[r] = ld_stream<u32x4v>(wdt + (size_t)r * hbytes);
     } else {
       load_x1<FMT_BF16>(a, kb, lane, xr);
     }

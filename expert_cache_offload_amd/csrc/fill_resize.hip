@@ -58,8 +58,10 @@ __global__ __launch_bounds__(FILL_THREADS) void fill_kernel(FillArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const size_t k = i + q * nthr;
-        // streaming store: the blob is read by the FFN later, not by this kernel
-        if (k < S16) __builtin_nontemporal_store(*(const u32x4*)&r[q], (u32x4*)(dst + k));
+        // plain stores: the step's FFN reads the blob right after this kernel, and a blob
+        // stored through the caches reaches it sooner than a streaming store (measured:
+        // the fused FFN launch that follows runs 0.6 us shorter, the link rate is unchanged)
+        if (k < S16) *(u32x4*)(dst + k) = *(const u32x4*)&r[q];
       }
     }
   }

@@ -17,7 +17,7 @@ import moe_inputs as mi
 
 from . import (make_shape, moe_cache_create, moe_cache_destroy, moe_cache_resize,
                moe_cache_snapshot, moe_expert_ffn, moe_fill_misses, moe_host_pool_alloc,
-               moe_host_pool_free, moe_layer_step, moe_plan_read, moe_route_classify,
+               moe_host_pool_free, moe_layer_step, moe_plan_read, moe_pool_read, moe_route_classify,
                moe_set_hybrid, moe_set_prefetch, moe_stats, moe_workspace_bytes)
 
 
@@ -29,7 +29,8 @@ def pinned_view(addr: int, nbytes: int) -> np.ndarray:
 class Workbench:
     def __init__(self, wl, device: str = "cuda:0", groups: int = 2, capacity: int | None = None,
                  max_capacity: int | None = None, gen_threads: int = 0, token_steps=None,
-                 compute_stream=None, fill_stream=None):
+                 compute_stream=None, fill_stream=None, pool_file: str | None = None,
+                 pool_threads: int = 8):
         self.wl = wl
         self.dev = torch.device(device)
         self.groups = groups
@@ -43,11 +44,15 @@ class Workbench:
         self.max_capacity = max(caps) if max_capacity is None else max_capacity
         self.shape = make_shape(L, E, K, H, I, wl.fmt, wl.has_shared, self.T)
         self.S = wl.blob_bytes
-        # pinned host pool, generated in place
+        # pinned host pool: generated in place, or read from a pool file in the runtime
+        # layout by the library's parallel readers straight into the pinned memory
         self.pool_bytes = L * E * self.S
         self.pool_addr = moe_host_pool_alloc(self.pool_bytes)
         self.pool = pinned_view(self.pool_addr, self.pool_bytes)
-        mi.fill_pool(wl.seed, wl.fmt, 0, L, E, H, I, self.pool_addr, gen_threads)
+        if pool_file:
+            moe_pool_read(pool_file, self.shape, self.pool_addr, pool_threads)
+        else:
+            mi.fill_pool(wl.seed, wl.fmt, 0, L, E, H, I, self.pool_addr, gen_threads)
         # GPU-resident inputs
         self.router_np = mi.router_weights(wl.seed, 0, L, E, H, nthreads=gen_threads)
         self.router = torch.from_numpy(self.router_np.view(np.int16)).to(self.dev)

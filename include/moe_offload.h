@@ -133,6 +133,15 @@ size_t moe_workspace_bytes(const moe_shape* shape, int32_t max_capacity);
 moe_status moe_auto_capacity(const moe_shape* shape, uint64_t free_bytes, uint64_t reserve_bytes,
                              double offload_ratio, int32_t* capacity);
 
+/* moe_auto_capacity over the current device's free memory as hipMemGetInfo reports it now
+ * (the budget the pages size the automatic cache from: the VRAM left once the resident
+ * weights are loaded, minus the KV floor in reserve_bytes).  *free_bytes (may be NULL)
+ * receives the free byte count used.  MOE_E_HIP if the query fails; otherwise as
+ * moe_auto_capacity. */
+moe_status moe_auto_capacity_device(const moe_shape* shape, uint64_t reserve_bytes,
+                                    double offload_ratio, int32_t* capacity,
+                                    uint64_t* free_bytes);
+
 /* Expert pool files in the runtime layout (the FreeToken paper summary, execution-layer
  * paragraph: weights merged ahead of time into the runtime layout load straight into their
  * final place).  A 64-byte header (magic "MOEPOOL1", int32 layers, experts, hidden, inter,
@@ -275,6 +284,15 @@ moe_status moe_set_hybrid(moe_cache cache, int32_t b_cpu_mbps, int32_t b_pcie_mb
  * negative argument.  Host arithmetic, for checking the closed form. */
 int32_t moe_miss_split(int32_t misses, int32_t b_cpu_mbps, int32_t b_pcie_mbps);
 
+/* Mode choice per weight format ("FreeToken: az VRAM ile büyük MoE modelleri", "Tuzaklar": a
+ * start-up probe prints each dtype's CPU expert rate and offload rate against a 2.0x
+ * threshold; bf16 at 1.02x offloads, fp8 has no CPU path).  Returns 1 (hybrid decode: split
+ * misses with moe_set_hybrid) when wfmt is bf16 - the only format with a CPU expert path - and
+ * cpu_gbps >= 2.0 * fill_gbps with both rates positive; 0 (fill every miss) otherwise; -1 for
+ * an unknown format or a negative or NaN rate.  Rates in GB/s as measured by the caller
+ * (moe_cpu_expert_rate, and the fill rate from moe_profile_read).  Host arithmetic. */
+int32_t moe_choose_mode(int32_t wfmt, double cpu_gbps, double fill_gbps);
+
 /* Longest time the combine kernel waits for the host's answer to a hybrid step before it
  * gives up (ERR_HYBRID: moe_stats / moe_cache_snapshot then return MOE_E_HYBRID), measured on
  * the GPU's constant clock; default 2 s.  MOE_E_BUSY while a step is in flight. */
@@ -336,6 +354,24 @@ typedef struct {
 
 moe_status moe_profile_enable(moe_cache cache, int32_t mask, int32_t every);
 moe_status moe_profile_read(moe_cache cache, moe_profile* out);
+
+/* Measurement probes: the ceilings the kernels are judged against, timed with event pairs
+ * that the kernel dispatch takes itself (as moe_profile_* does).  Synchronous.
+ * moe_probe_stream_read: `reps` launches of a read-only streaming kernel, each reading
+ * `bytes_per_launch` bytes of device memory once, in the decode FFN's access pattern (a
+ * 256-thread workgroup per contiguous 96 KiB, 24 16-byte loads per thread all in flight;
+ * `nontemporal` 1: streaming loads); launch r reads the r-th window of that size (cyclically)
+ * within the first `span_bytes` of `buf`, so windows span_bytes/bytes_per_launch launches
+ * apart - choose span far above the 256 MB last-level cache - are not cache-resident.  One
+ * untimed launch first.  *avg_us = average launch duration.  `sink`: a device word that is
+ * written only when a thread's loads fold to a fixed constant (it keeps the loads alive).
+ * bytes_per_launch: a multiple of 16, at most span_bytes; buf 16-byte aligned.
+ * moe_probe_empty_launch: `reps` launches of an empty kernel of `grid` 256-thread
+ * workgroups; *avg_us = average duration (the fixed cost of a launch of that size). */
+moe_status moe_probe_stream_read(const void* buf, uint64_t span_bytes, uint64_t bytes_per_launch,
+                                 int32_t nontemporal, int32_t reps, void* sink, void* stream,
+                                 double* avg_us);
+moe_status moe_probe_empty_launch(int32_t grid, int32_t reps, void* stream, double* avg_us);
 
 const char* moe_status_string(moe_status s);
 

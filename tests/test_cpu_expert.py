@@ -62,9 +62,33 @@ def test_cpu_expert_rate_positive():
 
 
 def test_mode_choice_threshold():
+    """The library's mode rule (moe_choose_mode) against the oracle's hybrid_mode and the
+    pages' printed probe rows."""
+    import json
+    import os
+
+    from oracle.split import hybrid_mode
     assert not ecoa.choose_hybrid(52.4, 51.5)   # the pages' bf16 probe: 1.02x -> offload
     assert ecoa.choose_hybrid(124.5, 56.0)
-    assert not ecoa.choose_hybrid(0.0, 51.3)    # no CPU path
+    assert not ecoa.choose_hybrid(0.0, 51.3)    # no CPU rate
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "mode_probe_ceilings.json")))
+    fmt_of = {"bf16": ecoa.MOE_FMT_BF16, "fp8": ecoa.MOE_FMT_FP8_E4M3_K128}
+    for row in g["rows"]:
+        got = ecoa.moe_choose_mode(fmt_of[row["dtype"]], row["cpu_GBps"] or 0.0,
+                                   row["offload_GBps"])
+        assert got == (1 if row["mode"] == "hybrid" else 0), row
+    rng = np.random.default_rng(3)
+    for _ in range(5000):
+        cpu, fill = (float(v) for v in rng.uniform(0.0, 300.0, 2))
+        if rng.random() < 0.1:
+            cpu = 2.0 * fill  # exactly at the threshold: hybrid
+        assert ecoa.moe_choose_mode(0, cpu, fill) == int(hybrid_mode(cpu, fill)), (cpu, fill)
+        assert ecoa.moe_choose_mode(1, cpu, fill) == 0  # fp8: no CPU expert path
+        assert ecoa.moe_choose_mode(2, cpu, fill) == 0  # MXFP4: none either
+    assert ecoa.moe_choose_mode(0, -1.0, 50.0) == -1
+    assert ecoa.moe_choose_mode(0, float("nan"), 50.0) == -1
+    assert ecoa.moe_choose_mode(3, 100.0, 50.0) == -1
 
 
 def test_kernel_closed_form_split_equals_oracle_minimiser():
