@@ -224,7 +224,8 @@ def read_probes(dev, launch_bytes: int, grid: int) -> dict:
     FFN kernel's grid."""
     import torch
 
-    from expert_cache_offload_amd import moe_probe_empty_launch, moe_probe_stream_read
+    from expert_cache_offload_amd import (moe_probe_copy, moe_probe_empty_launch,
+                                          moe_probe_stream_read)
     buf = torch.empty(PROBE_SPAN, dtype=torch.uint8, device=dev)
     buf.fill_(3)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
@@ -244,6 +245,9 @@ def read_probes(dev, launch_bytes: int, grid: int) -> dict:
     out["read_GBps"] = max(out["read_4GiB_plain_GBps"], out["read_4GiB_nt_GBps"])
     if launch_bytes >= 16:
         out["read_launch_GBps"] = max(out["read_launch_plain_GBps"], out["read_launch_nt_GBps"])
+    half = PROBE_SPAN // 2  # 2 GiB copied from the buffer's first half to its second
+    us = moe_probe_copy(buf, buf.data_ptr() + half, half, 4)
+    out["copy_2GiB_GBps"] = round(2 * half / us / 1e3, 1)  # bytes read + written
     out["empty_launch_us"] = round(moe_probe_empty_launch(max(1, grid), 200), 3)
     out["empty_launch_grid"] = grid
     del buf, sink
@@ -769,19 +773,17 @@ def pmc_summary(args) -> None:
          if r.get("Counter_Name") == "FETCH_SIZE"]
     W = [r for r in _csv_rows(write_dir, "counter_collection.csv")
          if r.get("Counter_Name") == "WRITE_SIZE"]
-    calib = [float(r["Counter_Value"]) * 1024 / PROBE_SPAN for r in F
-             if "stream_read_kernel" in _kname(r) and
-             float(r["Counter_Value"]) * 1024 > 0.5 * PROBE_SPAN * 0.25]
-    calib.sort()
+    # the library's plain copy probe in the same runs: 2 GiB read and 2 GiB written
+    cb = PROBE_SPAN // 2
+    calib = sorted(float(r["Counter_Value"]) * 1024 / cb for r in F
+                   if "stream_copy_kernel" in _kname(r))
     ff = calib[len(calib) // 2] if calib else 1.0
-    # writes: the probe buffer's 4 GiB fill (a torch fill kernel) in the same run
-    wcal = sorted(float(r["Counter_Value"]) * 1024 / PROBE_SPAN for r in W
-                  if "FillFunctor" in _kname(r) and
-                  float(r["Counter_Value"]) * 1024 > 0.2 * PROBE_SPAN)
+    wcal = sorted(float(r["Counter_Value"]) * 1024 / cb for r in W
+                  if "stream_copy_kernel" in _kname(r))
     fw = wcal[len(wcal) // 2] if wcal else 1.0
-    print(f"calibration: FETCH_SIZE of the 4 GiB probe reads / true bytes read: "
-          f"{[round(c, 4) for c in calib]} -> factor {ff:.4f}; WRITE_SIZE of the 4 GiB probe "
-          f"buffer fill / true bytes written: {[round(c, 4) for c in wcal]} -> factor {fw:.4f}")
+    print(f"calibration (plain copy probe, 2 GiB read + 2 GiB written per launch): FETCH_SIZE / "
+          f"bytes read {[round(c, 4) for c in calib]} -> factor {ff:.4f}; WRITE_SIZE / bytes "
+          f"written {[round(c, 4) for c in wcal]} -> factor {fw:.4f}")
     agg = {}
     for r in F:
         a = agg.setdefault(_kname(r), [0, 0.0, 0, 0.0])

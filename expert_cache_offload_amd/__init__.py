@@ -103,6 +103,8 @@ _SIGS = {
     "moe_probe_stream_read": (_i32, [_vp, ctypes.c_uint64, ctypes.c_uint64, _i32, _i32, _vp,
                                      _vp, ctypes.POINTER(ctypes.c_double)]),
     "moe_probe_empty_launch": (_i32, [_i32, _i32, _vp, ctypes.POINTER(ctypes.c_double)]),
+    "moe_probe_copy": (_i32, [_vp, _vp, ctypes.c_uint64, _i32, _vp,
+                              ctypes.POINTER(ctypes.c_double)]),
     "moe_set_hybrid_timeout": (_i32, [_vp, _i64]),
     "moe_hybrid_hold": (_i32, [_vp, _i32]),
     "moe_hybrid_read": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
@@ -359,6 +361,14 @@ def moe_probe_stream_read(buf, span_bytes: int, bytes_per_launch: int, nontempor
     _check(_lib.moe_probe_stream_read(_p(buf), int(span_bytes), int(bytes_per_launch),
                                       int(bool(nontemporal)), int(reps), _p(sink), stream,
                                       ctypes.byref(us)), "moe_probe_stream_read")
+    return float(us.value)
+
+
+def moe_probe_copy(src, dst, nbytes: int, reps: int, stream: int = 0) -> float:
+    """Average duration (us) of a plain device copy of nbytes (see the header)."""
+    us = ctypes.c_double(0.0)
+    _check(_lib.moe_probe_copy(_p(src), _p(dst), int(nbytes), int(reps), stream,
+                               ctypes.byref(us)), "moe_probe_copy")
     return float(us.value)
 
 

@@ -49,6 +49,8 @@ hipError_t launch_prefetch_plan(const Dims& d, const Dev& v, int layer, hipStrea
 hipError_t probe_stream_read(const void* buf, size_t span, size_t bytes, int nt, int reps,
                              uint32_t* sink, hipStream_t s, double* avg_us);
 hipError_t probe_empty_launch(int grid, int reps, hipStream_t s, double* avg_us);
+hipError_t probe_copy(const void* src, void* dst, size_t bytes, int reps, hipStream_t s,
+                      double* avg_us);
 }  // namespace moe
 
 using namespace moe;
@@ -810,6 +812,20 @@ moe_status moe_probe_stream_read(const void* buf, uint64_t span_bytes, uint64_t 
   if (nontemporal != 0 && nontemporal != 1) return MOE_E_INVALID;
   const hipError_t e = probe_stream_read(buf, span_bytes, bytes_per_launch, nontemporal, reps,
                                          (uint32_t*)sink, (hipStream_t)stream, avg_us);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_E_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t reps, void* stream,
+                          double* avg_us) {
+  if (!src || !dst || !avg_us || reps < 1 || reps > 100000) return MOE_E_INVALID;
+  if (!aligned16(src) || !aligned16(dst) || bytes < 16 || bytes % 16) return MOE_E_INVALID;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_E_INVALID;  // overlapping
+  const hipError_t e = probe_copy(src, dst, bytes, reps, (hipStream_t)stream, avg_us);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return MOE_E_HIP;

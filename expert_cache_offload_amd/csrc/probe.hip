@@ -42,6 +42,24 @@ __global__ __launch_bounds__(PRB_T) void stream_read_kernel(const u32x4p* p, lon
 
 __global__ __launch_bounds__(PRB_T) void empty_kernel() {}
 
+// Plain device copy of n16 16-byte chunks: the reference kernel of known read and write bytes
+// against which hardware byte counters are calibrated.
+__global__ __launch_bounds__(PRB_T) void stream_copy_kernel(const u32x4p* src, u32x4p* dst,
+                                                            long long n16) {
+  const long long base = (long long)blockIdx.x * (PRB_T * 8) + threadIdx.x;
+  u32x4p r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const long long k = base + (long long)i * PRB_T;
+    r[i] = src[k < n16 ? k : n16 - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const long long k = base + (long long)i * PRB_T;
+    if (k < n16) dst[k] = r[i];
+  }
+}
+
 // Average event-timed duration (us) of `reps` launches reading `bytes` each, launch r reading
 // the r-th window of `bytes` (cyclically) inside the first `span` bytes of `buf`; one untimed
 // launch first.  Synchronous.
@@ -63,6 +81,30 @@ hipError_t probe_stream_read(const void* buf, size_t span, size_t bytes, int nt,
   };
   if (e == hipSuccess) e = launch(reps, nullptr, nullptr);
   for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch(r, ev[2 * r], ev[2 * r + 1]);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  double sum = 0.0;
+  for (int r = 0; r < reps && e == hipSuccess; ++r) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]);
+    sum += ms;
+  }
+  for (auto& x : ev)
+    if (x) (void)hipEventDestroy(x);
+  if (e == hipSuccess) *avg_us = sum * 1e3 / reps;
+  return e;
+}
+
+hipError_t probe_copy(const void* src, void* dst, size_t bytes, int reps, hipStream_t s,
+                      double* avg_us) {
+  const long long n16 = (long long)(bytes / 16);
+  const int grid = (int)((n16 + PRB_T * 8 - 1) / (PRB_T * 8));
+  std::vector<hipEvent_t> ev(2 * (size_t)reps, nullptr);
+  hipError_t e = hipSuccess;
+  for (auto& x : ev)
+    if (e == hipSuccess) e = hipEventCreate(&x);
+  for (int r = 0; r < reps && e == hipSuccess; ++r)
+    e = launch_timed(stream_copy_kernel, dim3(grid), dim3(PRB_T), 0, s, ev[2 * r], ev[2 * r + 1],
+                     (const u32x4p*)src, (u32x4p*)dst, n16);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   double sum = 0.0;
   for (int r = 0; r < reps && e == hipSuccess; ++r) {

@@ -372,6 +372,12 @@ moe_status moe_probe_stream_read(const void* buf, uint64_t span_bytes, uint64_t 
                                  int32_t nontemporal, int32_t reps, void* sink, void* stream,
                                  double* avg_us);
 moe_status moe_probe_empty_launch(int32_t grid, int32_t reps, void* stream, double* avg_us);
+/* moe_probe_copy: `reps` launches of a plain copy kernel (16-byte loads and stores, every byte
+ * read once and written once) of `bytes` from src to dst (device memory, 16-byte aligned, not
+ * overlapping; bytes a multiple of 16); *avg_us = average launch duration.  The reference of
+ * known read and write bytes for calibrating hardware byte counters. */
+moe_status moe_probe_copy(const void* src, void* dst, uint64_t bytes, int32_t reps, void* stream,
+                          double* avg_us);
 
 const char* moe_status_string(moe_status s);
 
