@@ -210,6 +210,14 @@ __device__ __forceinline__ V ld_stream(const unsigned char* p) {
   return __builtin_nontemporal_load((const V*)p);
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads still in flight (the weight
+// stream) stay in flight across it, where __syncthreads would wait for every one of them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w),
                                          __builtin_bit_cast(bf16x2v, x), acc, false);
@@ -312,24 +320,27 @@ struct GuX {  // 16-byte activation vectors per weight chunk
 };
 
 // At one token: the lane's activations of pass kb (gate chunks c = (kb + k) * 64 + lane).
+// xrow: the token's activation row ([H] bf16).
 template <int FMT>
 __device__ __forceinline__ void load_x1(const FfnArgs& a, int kb, int lane,
-                                        u32x4v (&xr)[GN][GuX<FMT>::XV]) {
+                                        u32x4v (&xr)[GN][GuX<FMT>::XV], const uint16_t* xrow) {
   constexpr int EPL = Fmt<FMT>::EPL, XV = GuX<FMT>::XV;
   const int ngq = a.d.H / EPL;
 #pragma unroll
   for (int k = 0; k < GN; ++k) {
     int c = (kb + k) * 64 + lane;
     c = c < ngq ? c : ngq - 1;
-    const u32x4v* p = (const u32x4v*)(a.x + (size_t)c * EPL);
+    const u32x4v* p = (const u32x4v*)(xrow + (size_t)c * EPL);
 #pragma unroll
     for (int q = 0; q < XV; ++q) xr[k][q] = p[q];
   }
 }
 
+// xrow (NTOK == 1): the activation row of the entry's one token, for passes after the first.
 template <int FMT, int NTOK>
 __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
-                             u32x4v (&xr)[GN][GuX<FMT>::XV], uint16_t* s_x) {
+                             u32x4v (&xr)[GN][GuX<FMT>::XV], uint16_t* s_x,
+                             const uint16_t* xrow) {
   using F = Fmt<FMT>;
   constexpr int EPL = F::EPL, XV = GuX<FMT>::XV;
   const Dims& d = a.d;
@@ -357,9 +368,30 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
   float g0[NTOK], u0[NTOK], g1[NTOK], u1[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) g0[t] = u0[t] = g1[t] = u1[t] = 0.f;
+  constexpr int PC = GN * 64;                           // chunk slots per token per pass
+  constexpr int NSV = NTOK > 1 ? NTOK * PC * GuX<FMT>::XV / FT : 1;  // staged vectors/thread
   for (int kb = 0; kb * 64 < ngq; kb += GN) {
     u32x4v wg0[GN], wu0[GN], wg1[GN], wu1[GN];
     float sg0[GN], su0[GN], sg1[GN], su1[GN];  // block scales (fp8, MXFP4)
+    u32x4v sv[NSV];
+    if constexpr (NTOK > 1) {
+      // the pass's activations of every routed token, staged in LDS as [t][GN * 64 chunks of
+      // EPL] (rows past the entry's tokens repeat its first token): their loads go out first,
+      // then the weight stream, so the LDS stores wait for the activations alone
+      lds_barrier();  // the previous pass is done with s_x
+#pragma unroll
+      for (int q = 0; q < NSV; ++q) {
+        const int idx = (int)threadIdx.x + q * FT;
+        const int t = idx / (PC * XV), r = idx % (PC * XV);
+        const int c = kb * 64 + r / XV;
+        const int cc = c < ngq ? c : ngq - 1;
+        const int tt = t < ntok ? t : 0;
+        int tk = tok[0];
+#pragma unroll
+        for (int q2 = 1; q2 < NTOK; ++q2) tk = tt == q2 ? tok[q2] : tk;
+        sv[q] = *(const u32x4v*)(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < GN; ++k) {
       int c = (kb + k) * 64 + lane;
@@ -381,23 +413,12 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
       }
     }
     if constexpr (NTOK == 1) {
-      if (kb > 0) load_x1<FMT>(a, kb, lane, xr);
+      if (kb > 0) load_x1<FMT>(a, kb, lane, xr, xrow);
     } else {
-      // stage the pass's activations of every routed token: [t][GN * 64 chunks of EPL]
-      __syncthreads();  // previous pass done with s_x
-      constexpr int PC = GN * 64;  // chunks per token per pass
-      for (int idx = threadIdx.x; idx < NTOK * PC * XV; idx += FT) {
-        const int t = idx / (PC * XV), r = idx % (PC * XV);
-        const int c = kb * 64 + r / XV;
-        const int cc = c < ngq ? c : ngq - 1;
-        const int tt = t < ntok ? t : 0;
-        int tk = tok[0];
 #pragma unroll
-        for (int q = 1; q < NTOK; ++q) tk = tt == q ? tok[q] : tk;
-        const u32x4v v = *(const u32x4v*)(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8);
-        *(u32x4v*)(s_x + ((size_t)t * PC * XV + r) * 8) = v;
-      }
-      __syncthreads();
+      for (int q = 0; q < NSV; ++q)
+        *(u32x4v*)(s_x + ((size_t)threadIdx.x + (size_t)q * FT) * 8) = sv[q];
+      lds_barrier();
     }
 #pragma unroll
     for (int k = 0; k < GN; ++k) {
@@ -558,7 +579,7 @@ __device__ void down_role(const FfnArgs& a, const Entry& en, int cb, int rs, uns
       const int idx = threadIdx.x + q * FT;
       if (idx < NTOK * IR) s_act[idx] = sv[q];
     }
-    __syncthreads();
+    lds_barrier();  // the weight rows stay in flight
   }
   float acc[NTOK][DC];
 #pragma unroll
@@ -745,7 +766,7 @@ __device__ void fused_role(const FfnArgs& a, const Entry& en, int rb, u32x4v (&x
 #pragma unroll
       for (int r = 0; r < NR; ++r) wd[r] = ld_stream<u32x4v>(wdt + (size_t)r * hbytes);
     } else {
-      load_x1<FMT_BF16>(a, kb, lane, xr);
+      load_x1<FMT_BF16>(a, kb, lane, xr, a.x);
     }
 #pragma unroll
     for (int k = 0; k < GN; ++k) {
@@ -766,7 +787,7 @@ __device__ void fused_role(const FfnArgs& a, const Entry& en, int rb, u32x4v (&x
   wave_reduce_units<1>(gv, uv, lane);
   if ((lane & 31) == 0)  // lane 0 holds row i0, lane 32 row i1
     s_a[lane == 0 ? wave : wave + FR / 2] = silu(gv[0]) * uv[0] * wt;
-  __syncthreads();
+  lds_barrier();  // the WdT rows may still be arriving
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -860,11 +881,27 @@ __global__ __launch_bounds__(FT) void ffn_gate_up_kernel(FfnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nra = a.d.I / RA;
   u32x4v xr[GN][GuX<FMT>::XV];
-  // at one token the activations do not depend on the plan: they go out before the entry
-  if constexpr (NTOK == 1) load_x1<FMT>(a, 0, threadIdx.x & 63, xr);
-  Entry en;
-  if (!resolve(a, blockIdx.x / nra, en)) return;
-  gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra, xr, (uint16_t*)smem);
+  if constexpr (NTOK == 1) {
+    // at one token the activations do not depend on the plan: they go out before the entry
+    load_x1<FMT>(a, 0, threadIdx.x & 63, xr, a.x);
+    Entry en;
+    if (!resolve(a, blockIdx.x / nra, en)) return;
+    gate_up_role<FMT, 1>(a, en, blockIdx.x % nra, xr, nullptr, a.x);
+  } else {
+    Entry en;
+    if (!resolve(a, blockIdx.x / nra, en)) return;
+    if (FMT != FMT_MXFP4 && en.ntok == 1 && !en.shared) {
+      // an expert that one token of the step uses (the common case across streams): that
+      // token's activations in registers, as at one token, with no staging in LDS (not for
+      // e2m1 weights, whose 16-byte chunk needs 64 bytes of activations: there the four waves
+      // share one staged copy)
+      const uint16_t* xrow = a.x + (size_t)a.v.row_tok[en.row0] * a.d.H;
+      load_x1<FMT>(a, 0, threadIdx.x & 63, xr, xrow);
+      gate_up_role<FMT, 1>(a, en, blockIdx.x % nra, xr, nullptr, xrow);
+    } else {
+      gate_up_role<FMT, NTOK>(a, en, blockIdx.x % nra, xr, (uint16_t*)smem, nullptr);
+    }
+  }
 }
 
 template <int FMT, int NTOK>
@@ -892,7 +929,7 @@ __global__ __launch_bounds__(FFT, FWPE) void ffn_fused_kernel(FfnArgs a) {
   const int nrb = a.d.I / FR;
   u32x4v xr[GN][1];
   // the activations do not depend on the plan: they go out before the entry
-  load_x1<FMT_BF16>(a, 0, threadIdx.x & 63, xr);
+  load_x1<FMT_BF16>(a, 0, threadIdx.x & 63, xr, a.x);
   Entry en;
   if (!resolve(a, blockIdx.x / nrb, en)) return;  // uniform per workgroup
   fused_role<NR>(a, en, blockIdx.x % nrb, xr, s_a, (float*)smem);
