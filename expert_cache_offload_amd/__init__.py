@@ -86,6 +86,7 @@ _SIGS = {
     "moe_expert_ffn": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp]),
     "moe_layer_step": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "moe_cache_snapshot": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_cache_set_step": (_i32, [_vp, _i64]),
     "moe_plan_read": (_i32, [_vp, ctypes.POINTER(MoePlanHost)]),
     "moe_stats": (_i32, [_vp, ctypes.POINTER(MoeCounters)]),
     "moe_profile_enable": (_i32, [_vp, _i32, _i32]),
@@ -222,7 +223,7 @@ def moe_cache_snapshot(handle: int, capacity: int, n_keys: int):
     """Returns (key_of, stamp, slot_of, n, step, capacity) as numpy arrays / ints."""
     import numpy as np
     key_of = np.empty(capacity, np.int32)
-    stamp = np.empty(capacity, np.int32)
+    stamp = np.empty(capacity, np.int64)
     slot_of = np.empty(n_keys, np.int32)
     n = ctypes.c_int32()
     step = ctypes.c_int64()
@@ -232,6 +233,11 @@ def moe_cache_snapshot(handle: int, capacity: int, n_keys: int):
                                  ctypes.addressof(step), ctypes.addressof(cap))
     _check(st, "moe_cache_snapshot", handle)
     return key_of[:cap.value], stamp[:cap.value], slot_of, n.value, step.value, cap.value
+
+
+def moe_cache_set_step(handle: int, step: int) -> None:
+    """Set the step counter of an empty cache (see the header)."""
+    _check(_lib.moe_cache_set_step(handle, int(step)), "moe_cache_set_step", handle)
 
 
 def moe_plan_read(handle: int, max_unique: int, max_assign: int) -> dict:

@@ -111,7 +111,7 @@ Layout make_layout(const Dims& d) {
   };
   const size_t I4 = sizeof(int32_t);
   L.key_of = take(I4 * d.max_capacity);
-  L.stamp = take(I4 * d.max_capacity);
+  L.stamp = take(sizeof(int64_t) * d.max_capacity);
   L.slot_of = take(I4 * (size_t)d.L * d.E);
   L.ctrl = take(I4 * CTRL_WORDS);
   L.stats = take(sizeof(uint64_t) * STAT_WORDS);
@@ -162,7 +162,7 @@ Dev make_dev(void* ws, const Layout& L) {
   char* b = (char*)ws;
   Dev v{};
   v.key_of = (int*)(b + L.key_of);
-  v.stamp = (int*)(b + L.stamp);
+  v.stamp = (long long*)(b + L.stamp);
   v.slot_of = (int*)(b + L.slot_of);
   v.ctrl = (int*)(b + L.ctrl);
   v.stats = (unsigned long long*)(b + L.stats);
@@ -1030,14 +1030,14 @@ moe_status moe_layer_step(moe_cache c, int32_t layer, const void* x, int32_t T,
   return moe_expert_ffn(c, layer, x, T, shared_blob, y, compute_stream);
 }
 
-moe_status moe_cache_snapshot(moe_cache c, int32_t* key_of, int32_t* stamp, int32_t* slot_of,
+moe_status moe_cache_snapshot(moe_cache c, int32_t* key_of, int64_t* stamp, int32_t* slot_of,
                               int32_t* n_occupied, int64_t* step, int32_t* capacity) {
   if (!c) return MOE_E_INVALID;
   if (c->state != State::Idle) return MOE_E_BUSY;
   hipError_t e = hipDeviceSynchronize();
   const size_t cap = (size_t)c->capacity;
   if (e == hipSuccess && key_of) e = hipMemcpy(key_of, c->v.key_of, 4 * cap, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && stamp) e = hipMemcpy(stamp, c->v.stamp, 4 * cap, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && stamp) e = hipMemcpy(stamp, c->v.stamp, 8 * cap, hipMemcpyDeviceToHost);
   if (e == hipSuccess && slot_of)
     e = hipMemcpy(slot_of, c->v.slot_of, 4 * (size_t)c->d.L * c->d.E, hipMemcpyDeviceToHost);
   int ctrl[CTRL_WORDS];
@@ -1048,6 +1048,21 @@ moe_status moe_cache_snapshot(moe_cache c, int32_t* key_of, int32_t* stamp, int3
   if (capacity) *capacity = ctrl[CTRL_C];
   if (ctrl[CTRL_ERR] & ERR_CAPACITY) return MOE_E_CAPACITY;
   if (ctrl[CTRL_ERR] & ERR_HYBRID) return MOE_E_HYBRID;
+  return MOE_OK;
+}
+
+moe_status moe_cache_set_step(moe_cache c, int64_t step) {
+  if (!c || step < 0) return MOE_E_INVALID;
+  if (c->state != State::Idle || c->pf_layer[0] >= 0 || c->pf_layer[1] >= 0) return MOE_E_BUSY;
+  hipError_t e = hipDeviceSynchronize();
+  int ctrl[CTRL_WORDS];
+  if (e == hipSuccess) e = hipMemcpy(ctrl, c->v.ctrl, sizeof(ctrl), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e);
+  if (ctrl[CTRL_N] != 0) return MOE_E_INVALID;  // cached stamps would no longer precede it
+  const int w[2] = {(int)(step & 0xffffffff), (int)(step >> 32)};
+  e = hipMemcpy(c->v.ctrl + CTRL_STEP_LO, w, sizeof(w), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(c, e);
   return MOE_OK;
 }
 

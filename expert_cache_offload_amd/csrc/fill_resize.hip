@@ -143,15 +143,18 @@ __global__ __launch_bounds__(RZ) void resize_plan_kernel(ResizeArgs a) {
   // Sort the n occupied slots by (stamp, key) ascending: bitonic sort in LDS.
   int P = 1;
   while (P < n) P <<= 1;
-  uint64_t* s_key = (uint64_t*)smem;       // [P] (stamp << 32 | key)
+  uint64_t* s_st = (uint64_t*)smem;       // [P] 64-bit stamps
+  uint32_t* s_key = (uint32_t*)(s_st + P);  // [P] keys
   int* s_slot = (int*)(s_key + P);        // [P]
   int* s_evict = s_slot + P;              // [max_capacity] 1 = evicted
   for (int i = threadIdx.x; i < P; i += RZ) {
     if (i < n) {
-      s_key[i] = ((uint64_t)(uint32_t)v.stamp[i] << 32) | (uint32_t)v.key_of[i];
+      s_st[i] = (uint64_t)v.stamp[i];
+      s_key[i] = (uint32_t)v.key_of[i];
       s_slot[i] = i;
     } else {
-      s_key[i] = ~0ull;
+      s_st[i] = ~0ull;
+      s_key[i] = ~0u;
       s_slot[i] = -1;
     }
   }
@@ -163,8 +166,12 @@ __global__ __launch_bounds__(RZ) void resize_plan_kernel(ResizeArgs a) {
         const int l = i ^ jj;
         if (l > i) {
           const bool up = (i & k) == 0;
-          const uint64_t ki = s_key[i], kl = s_key[l];
-          if ((ki > kl) == up) {
+          const uint64_t si = s_st[i], sl = s_st[l];
+          const uint32_t ki = s_key[i], kl = s_key[l];
+          const bool gt = si > sl || (si == sl && ki > kl);
+          if (gt == up) {
+            s_st[i] = sl;
+            s_st[l] = si;
             s_key[i] = kl;
             s_key[l] = ki;
             const int t = s_slot[i];
@@ -232,8 +239,8 @@ __global__ __launch_bounds__(RZ) void resize_plan_kernel(ResizeArgs a) {
 size_t resize_lds_bytes(int max_capacity) {
   int P = 1;
   while (P < max_capacity) P <<= 1;
-  return (size_t)P * (sizeof(uint64_t) + sizeof(int)) + sizeof(int) * (size_t)max_capacity * 2 +
-         64;
+  return (size_t)P * (sizeof(uint64_t) + 2 * sizeof(int)) +
+         sizeof(int) * (size_t)max_capacity * 2 + 64;
 }
 
 struct CopyArgs {

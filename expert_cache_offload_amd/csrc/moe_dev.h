@@ -2,7 +2,7 @@
 //
 // Workspace state (persistent across steps, device memory owned by the caller):
 //   key_of[max_capacity]  key held by each slot (key = layer*E + expert), -1 empty
-//   stamp[max_capacity]   global step of the slot's last use, -1 empty
+//   stamp[max_capacity]   global step of the slot's last use (64-bit), -1 empty
 //   slot_of[L*E]          slot of each key, -1 when not cached
 //   ctrl[16]              occupancy n, capacity C, step counter, error bits, tickets
 //   stats[8]              steps, hits, misses, bytes filled, FFN bytes, CPU misses, ...
@@ -115,7 +115,7 @@ __host__ __device__ inline size_t mail_bytes(int H) {
 
 struct Dev {
   int* key_of;
-  int* stamp;
+  long long* stamp;
   int* slot_of;
   int* ctrl;
   unsigned long long* stats;

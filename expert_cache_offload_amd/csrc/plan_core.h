@@ -55,7 +55,7 @@ __device__ inline uint64_t block_min_u64(uint64_t v, uint64_t* s_tmp) {
 
 // LDS arrays of the plan (dynamic shared memory).
 struct PlanLds {
-  uint64_t* comp;  // [max_capacity] (stamp << 32 | key) per occupied slot
+  uint64_t* comp;  // [max_capacity] 64-bit stamp per occupied slot (~0: not evictable)
   int* cnt;        // [E] assignments per expert this step
   int* uidx;       // [E] position of an expert in U, -1 if unused
   int* srow;       // [E] this layer's row of slot_of
@@ -136,7 +136,8 @@ constexpr int kRowsPerThread = 1024 / RT;  // slot_of row entries per thread (E 
 struct PlanState {
   int n, C;
   long long step;
-  uint32_t st[kSlotsPerThread], key[kSlotsPerThread];  // this thread's occupied slots
+  uint64_t st[kSlotsPerThread];   // this thread's slots: stamps (~0: empty) and keys
+  uint32_t key[kSlotsPerThread];
   int srow[kRowsPerThread];                            // this thread's slot_of row entries
 };
 
@@ -156,7 +157,7 @@ __device__ inline void plan_begin_load(const Dims& d, const Dev& v, int layer, P
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int i = (int)threadIdx.x + j * RT;
     const bool in = i < d.max_capacity;
-    ps.st[j] = in ? (uint32_t)v.stamp[i] : 0xffffffffu;
+    ps.st[j] = in ? (uint64_t)v.stamp[i] : ~0ull;
     ps.key[j] = in ? (uint32_t)v.key_of[i] : 0xffffffffu;
   }
 }
@@ -177,7 +178,7 @@ __device__ inline void plan_begin_store(const Dims& d, PlanLds& s, PlanState& ps
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int i = (int)threadIdx.x + j * RT;
     if (i >= ps.n) {
-      ps.st[j] = 0xffffffffu;
+      ps.st[j] = ~0ull;
       ps.key[j] = 0xffffffffu;
     }
   }
@@ -270,9 +271,9 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
   if (need > 0) {
     const uint64_t NONE = ~0ull;
 #pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j) {
+    for (int j = 0; j < kSlotsPerThread; ++j) {  // the keys stay in this thread's registers
       const int i = (int)threadIdx.x + j * RT;
-      if (i < n) s.comp[i] = ((uint64_t)ps.st[j] << 32) | ps.key[j];
+      if (i < n) s.comp[i] = ps.st[j];
     }
     __syncthreads();
     for (int u = threadIdx.x; u < nU; u += RT)  // keys of this step are never victims
@@ -282,6 +283,10 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
       if (sl >= 0 && sl < n) s.comp[sl] = NONE;
     }
     __syncthreads();
+    // group keys in collection order and in key order: the slot assignment's arrays, which
+    // are free until the victims are known
+    int* gkey = s.aslot;
+    int* skey = s.avkey;
     int got = 0;
     for (int round = 0; round < need && got < need; ++round) {
       uint64_t m = NONE;
@@ -291,29 +296,33 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
         if (threadIdx.x == 0) pt.err = 1;
         break;
       }
-      const uint32_t st = (uint32_t)(m >> 32);
       if (threadIdx.x == 0) pt.g = 0;
       __syncthreads();
-      for (int i = threadIdx.x; i < n; i += RT) {
-        const uint64_t c = s.comp[i];
-        if (c != NONE && (uint32_t)(c >> 32) == st) {
+#pragma unroll
+      for (int j = 0; j < kSlotsPerThread; ++j) {
+        const int i = (int)threadIdx.x + j * RT;
+        if (i < n && s.comp[i] == m) {
           const int q = atomicAdd(&pt.g, 1);
-          if (q < pw) s.grp[q] = i;
+          if (q < pw) {
+            s.grp[q] = i;
+            gkey[q] = (int)ps.key[j];
+          }
         }
       }
       __syncthreads();
       const int g = pt.g < pw ? pt.g : pw;
       for (int q = threadIdx.x; q < g; q += RT) {  // order the group by key
-        const uint32_t kq = (uint32_t)s.comp[s.grp[q]];
+        const int kq = gkey[q];
         int rank = 0;
-        for (int r = 0; r < g; ++r) rank += ((uint32_t)s.comp[s.grp[r]] < kq);
+        for (int r = 0; r < g; ++r) rank += (gkey[r] < kq);
         s.sorted[rank] = s.grp[q];
+        skey[rank] = kq;
       }
       __syncthreads();
       const int take = g < need - got ? g : need - got;
       for (int q = threadIdx.x; q < take; q += RT) {
         s.vict[got + q] = s.sorted[q];
-        s.vkey[got + q] = (int)(uint32_t)s.comp[s.sorted[q]];
+        s.vkey[got + q] = skey[q];
         s.comp[s.sorted[q]] = NONE;
       }
       got += take;
@@ -357,7 +366,7 @@ __device__ inline bool plan_cache(const Dims& d, const Dev& v, const PlanOut& o,
   }
   __syncthreads();
   for (int u = threadIdx.x; u < nU; u += RT) {
-    if (s.uslot[u] >= 0) v.stamp[s.uslot[u]] = (int)ps.step;  // CPU misses hold no slot
+    if (s.uslot[u] >= 0) v.stamp[s.uslot[u]] = ps.step;  // CPU misses hold no slot
     o.u_slot[u] = s.uslot[u];
     o.u_hit[u] = s.hit[u];
   }

@@ -236,12 +236,18 @@ moe_status moe_layer_step(moe_cache cache, int32_t layer, const void* x, int32_t
                           float* topk_w, void* y, int32_t groups, void* compute_stream,
                           void* fill_stream);
 
-/* Synchronous copies of the cache state: key_of[capacity], stamp[capacity] (step
+/* Synchronous copies of the cache state: key_of[capacity], stamp[capacity] (64-bit step
  * of last use, -1 empty), slot_of[layers*experts] (-1 absent), occupancy n and the
  * step counter.  Any pointer may be NULL. */
-moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int32_t* stamp,
+moe_status moe_cache_snapshot(moe_cache cache, int32_t* key_of, int64_t* stamp,
                               int32_t* slot_of, int32_t* n_occupied, int64_t* step,
                               int32_t* capacity);
+
+/* Sets the global step counter (the stamp the next layer step gives its experts; 64-bit, as
+ * are the stamps) of an empty cache, e.g. to carry a session's clock over into a new handle.
+ * Synchronous.  MOE_E_INVALID for step < 0 or a cache that holds any expert (their stamps
+ * would no longer precede the counter); MOE_E_BUSY while a step is in flight. */
+moe_status moe_cache_set_step(moe_cache cache, int64_t step);
 
 /* Prefetch mode for steps of more than 8 tokens (prefill chunks), whose routing union
  * covers nearly every expert (FreeToken paper summary, agihunt.info / arXiv 2608.16157,

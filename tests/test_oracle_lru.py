@@ -296,3 +296,23 @@ def test_prefetch_capacity_error_when_protected_fill_the_cache():
     c.step(0, [0, 1, 2, 3], E, 0)
     with pytest.raises(CapacityError):
         c.step(1, list(range(E)), E, 1, protected=[0, 1, 2, 3])
+
+
+def test_stamps_beyond_32_bits_change_nothing_but_the_stamps():
+    """The rule depends only on the order of stamps: the same accesses from a counter that
+    starts just below 2^32 (so that it crosses it) give the same hits, victims, slots and
+    occupancy as from 0, with every stamp shifted by the offset."""
+    import random
+    rng = random.Random(5)
+    E, L, C = 16, 3, 10
+    trace = [(s % L, sorted(rng.sample(range(E), rng.randint(1, 4)))) for s in range(300)]
+    off = (1 << 32) - 7
+    a, b = LRUCache(C, L * E), LRUCache(C, L * E)
+    for s, (l, U) in enumerate(trace):
+        if s == 150:
+            assert a.resize(6) == b.resize(6)
+        ra, rb = a.step(l, U, E, s), b.step(l, U, E, s + off)
+        assert (ra.hit, ra.slot, ra.misses, ra.key_of, ra.n) == (rb.hit, rb.slot, rb.misses,
+                                                                 rb.key_of, rb.n)
+        assert [x + off if x >= 0 else -1 for x in ra.stamp] == rb.stamp
+    assert max(b.stamp) > (1 << 32)
