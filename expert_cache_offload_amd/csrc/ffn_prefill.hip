@@ -9,21 +9,21 @@
 // turning this overlap off at about a quarter of prefill speed).
 //
 // Gfx950 design.  Dense contractions on v_mfma_f32_32x32x16_bf16 (fp32 accumulation):
-//   gate/up  - tile = 128 rows x 128 intermediate rows; the 256 GEMM columns are the 128
+//   gate/up  - tile = 256 rows x 128 intermediate rows; the 256 GEMM columns are the 128
 //              gate rows and the 128 up rows, so each wave holds gate and up of the same
 //              (row, i) in the same lane and the epilogue a = silu(g) * u * w is per lane;
-//              a wave owns 64 rows x 64 intermediate rows (eight 32 x 32 MFMA tiles: six
-//              16-byte LDS reads feed eight MFMAs); rows are gathered from x by the plan's
-//              row -> token map; a is stored bf16;
-//   down     - tile = 128 rows x 128 output columns over the stored transpose WdT, whose
+//              eight waves, each 64 rows x 64 intermediate rows (eight 32 x 32 MFMA tiles:
+//              six 16-byte LDS reads feed eight MFMAs); operands land in LDS by direct
+//              global-to-LDS loads; rows are gathered from x by the plan's row -> token map;
+//              a is stored bf16;
+//   down     - tile = 256 rows x 128 output columns over the stored transpose WdT, whose
 //              rows are contraction rows: the B tile is transposed on its way into LDS;
-//              fp32 partial rows per (token, choice);
+//              fp32 partial rows per (token, choice); four waves, 128 x 64 each;
 //   combine  - y[t] = bf16(sum over the token's k rows (+ shared) in a fixed order).
-// Four waves per workgroup in a 2 x 2 arrangement (down: 64 x 64 each, four 32 x 32 MFMA
-// tiles), a 64-wide contraction stage in LDS with the next stage's global loads in flight
-// during the MFMAs.  Workgroups are persistent over the launch's tiles, whose count depends on
-// the plan (read on the device): a prefix over the launch's entries maps a tile to its
-// expert, row tile and column tile.
+// A 64-wide contraction stage in LDS with the next stage's global loads in flight during the
+// MFMAs.  Workgroups are persistent over the launch's tiles, whose count depends on the plan
+// (read on the device): a prefix over the launch's entries maps a tile to its expert, row
+// tile and column tile.
 #include "moe_dev.h"
 
 namespace moe {
@@ -102,7 +102,7 @@ __device__ __forceinline__ PfEntry pf_entry(const PfArgs& a, int g) {
 template <int TBM>
 __device__ int pf_tile_prefix(const PfArgs& a, int* s_mt, int& first) {
   const int n = pf_launch_entries(a, first);
-  for (int j = threadIdx.x; j < n; j += PFT) {
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
     const PfEntry en = pf_entry(a, first + j);
     s_mt[j + 1] = (en.rows + TBM - 1) / TBM;
   }
@@ -136,23 +136,44 @@ __device__ __forceinline__ int xcd_order() {
 __device__ __forceinline__ uint16_t pf_bf16(float f) { return f32_to_bf16_rne(f); }
 
 // ---------------------------------------------------------------- gate / up
-// (two waves per SIMD: the accumulators and the stage's loads fit 256 registers per lane)
-__global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
-  __shared__ __align__(16) uint16_t As[BM * LDK];
-  __shared__ __align__(16) uint16_t Bs[2 * GBI * LDK];
+// Tile = 256 rows x 128 intermediate rows (256 GEMM columns: 128 gate rows, then the 128 up
+// rows of the same i), one workgroup of eight waves per CU in a 4 x 2 arrangement; a wave owns
+// 64 rows x 64 i: eight 32 x 32 MFMA tiles (two row tiles times gate and up times two column
+// tiles) fed by six 16-byte LDS reads per 16-deep step, the next step's reads issued before
+// this step's MFMAs.  Operands go from global memory straight into LDS (gfx950's 16-byte
+// global-to-LDS loads: no registers, no LDS store instructions) in two stages of 64
+// contraction elements (32 KiB of rows + 32 KiB of weights each) with one barrier per stage:
+// a stage's loads are issued right after the barrier that frees its buffer and land while the
+// other stage computes.  Rows are 128 bytes without padding; 16-byte chunk c of row r sits at
+// chunk c ^ (r & 7), so the eight lanes an LDS read serves together (eight rows, one chunk)
+// fall on distinct banks.  Rows past the expert's count load a valid row: they only reach
+// output rows that are never stored.
+constexpr int GU_T = 512;                         // threads (8 waves)
+constexpr int GU_BM = 256;                        // rows per gate/up tile
+constexpr int GU_STAGE = (GU_BM + 2 * GBI) * BK;  // bf16 elements per LDS stage
+constexpr int GU_LPW = GU_STAGE * 2 / (16 * 64) / (GU_T / 64);  // 1 KiB loads per wave per stage (8)
+
+__device__ __forceinline__ int gu_swz(int row, int chunk) {  // element offset of (row, chunk)
+  return row * BK + ((chunk ^ (row & 7)) << 3);
+}
+
+__global__ __launch_bounds__(GU_T, 1) void ffn_prefill_gate_up_kernel(PfArgs a) {
+  extern __shared__ __align__(16) uint16_t pf_smem[];  // 2 stages: [rows][BK] then [cols][BK]
   __shared__ int s_mt[kMaxEntriesPf + 1];
-  __shared__ float s_w[BM];  // routing weight of each row of the tile
+  __shared__ float s_w[GU_BM];  // routing weight of each row of the tile
   const Dims& d = a.d;
   const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int first;
-  const int n = pf_tile_prefix<BM>(a, s_mt, first);
+  const int n = pf_tile_prefix<GU_BM>(a, s_mt, first);
   const int NT = I / GBI;
   const int ntiles = s_mt[n] * NT;
-  // this thread's 16-byte chunks of each stage: A rows lr + 32 h (h < 4), B rows lr + 32 h
-  // (h < 8), columns lc .. lc + 8
-  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+  const int nst = H / BK;  // contraction stages
+  // global-to-LDS loads: load i of wave w fills LDS rows 8 (w * GU_LPW + i) .. + 7 of the
+  // stage (rows 0..255: x rows, 256..511: weight rows); lane l brings row ... + l / 8,
+  // physical chunk l % 8 = logical chunk lc ^ (row & 7)
+  const int lrow = lane >> 3, lc = (lane & 7) ^ lrow;
   for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
@@ -161,25 +182,28 @@ __global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
       atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
       if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_BLOB_BYTES], (unsigned long long)d.S);
     }
-    const int m0 = (mt - s_mt[j]) * BM;
+    const int m0 = (mt - s_mt[j]) * GU_BM;
     const int i0 = nt * GBI;
-    if ((int)threadIdx.x < BM) {  // read by the epilogue, after the k loop's barriers
+    if ((int)threadIdx.x < GU_BM) {  // read by the epilogue, after the k loop's barriers
       const int r = m0 + threadIdx.x;
       s_w[threadIdx.x] = r >= en.rows ? 0.f : en.shared ? 1.0f : a.v.row_w[en.row0 + r];
     }
-    // A rows (gathered tokens); rows past the expert's count read zeros
-    const uint16_t* arow[4];
-    bool aval[4];
+    // this lane's GU_LPW source rows: x rows gathered by token (T * H < 2^31), weight rows
+    // (tile column c < GBI: gate row i0 + c, else up row i0 + c - GBI)
+    const uint16_t* src[GU_LPW];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int r = m0 + lr + 32 * h;
-      aval[h] = r < en.rows;
-      const int tok = !aval[h] ? 0 : en.shared ? r : a.v.row_tok[en.row0 + r];
-      arow[h] = a.x + (size_t)tok * H;
+    for (int i = 0; i < GU_LPW; ++i) {
+      const int row = (wave * GU_LPW + i) * 8 + lrow;  // stage row 0 .. 511
+      if (row < GU_BM) {
+        const int r = m0 + row;
+        const int tok = r >= en.rows ? (en.shared ? 0 : a.v.row_tok[en.row0]) :
+                        en.shared ? r : a.v.row_tok[en.row0 + r];
+        src[i] = a.x + (size_t)tok * H + lc * 8;
+      } else {
+        const int col = row - GU_BM, g = col >> 7, c = col & (GBI - 1);
+        src[i] = (const uint16_t*)en.blob + (size_t)(2 * (i0 + c) + g) * H + lc * 8;
+      }
     }
-    // B rows: tile column c = lr + 32 h < GBI is gate row i0 + c, c >= GBI is up row
-    // i0 + c - GBI; one base pointer and workgroup-uniform offsets (h & 3) * 64 H + (h >> 2) H
-    const uint16_t* bbase = (const uint16_t*)en.blob + (size_t)(i0 + lr) * 2 * H;
     f32x16_t acc[2][2][2];  // [row tile][gate, up][column tile]
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
@@ -189,51 +213,50 @@ __global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
           for (int q = 0; q < 16; ++q) acc[rr][g][cc][q] = 0.f;
-    u32x4_t ra[4], rb[8];
-    const u32x4_t z4 = {0u, 0u, 0u, 0u};
-    // loads are unconditional (rows past the count read a valid row) and masked when they
-    // are stored to LDS: a conditional load would make the compiler wait for it at once
+    auto load_stage = [&](int st, int buf) {
+      uint16_t* dst = pf_smem + buf * GU_STAGE + wave * GU_LPW * 8 * BK;
+      const int k0 = st * BK;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) ra[h] = *(const u32x4_t*)(arow[h] + lc);
-#pragma unroll
-    for (int h = 0; h < 8; ++h)
-      rb[h] = *(const u32x4_t*)(bbase + (size_t)((h & 3) * 64 + (h >> 2)) * H + lc);
-    for (int k0 = 0; k0 < H; k0 += BK) {
-      __syncthreads();  // the previous stage's MFMAs are done with the LDS tiles
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = aval[h] ? ra[h] : z4;
-#pragma unroll
-      for (int h = 0; h < 8; ++h) *(u32x4_t*)(Bs + (lr + 32 * h) * LDK + lc) = rb[h];
-      __syncthreads();
-      const int kn = k0 + BK < H ? k0 + BK : k0;  // last stage: harmless reload
-#pragma unroll
-      for (int h = 0; h < 4; ++h) ra[h] = *(const u32x4_t*)(arow[h] + kn + lc);
-#pragma unroll
-      for (int h = 0; h < 8; ++h)
-        rb[h] = *(const u32x4_t*)(bbase + (size_t)((h & 3) * 64 + (h >> 2)) * H + kn + lc);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += 16) {
-        const int ko = kk + 8 * (lane >> 5);
-        bf16x8_t af[2], bf[2][2];
+      for (int i = 0; i < GU_LPW; ++i)
+        __builtin_amdgcn_global_load_lds(src[i] + k0, dst + i * 8 * BK, 16, 0, 0);
+    };
+    load_stage(0, 0);
+    load_stage(1, 1);  // H >= 256: at least 4 stages
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt <= 8: stage 0 has landed
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      const uint16_t* As = pf_smem + (st & 1) * GU_STAGE;
+      const uint16_t* Bs = As + GU_BM * BK;
+      bf16x8_t af[2][2], bf[2][2][2];  // [step parity][...]
+      auto read_frags = [&](int kk, int p) {
+        const int ch = 2 * kk + (lane >> 5);  // 16-byte chunk of this lane's operands
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
-          af[rr] = *(const bf16x8_t*)(As + (wm * 64 + rr * 32 + (lane & 31)) * LDK + ko);
+          af[p][rr] = *(const bf16x8_t*)(As + gu_swz(wm * 64 + rr * 32 + (lane & 31), ch));
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc)
-            bf[g][cc] = *(const bf16x8_t*)(Bs + (g * GBI + wn * 64 + cc * 32 + (lane & 31)) * LDK + ko);
+            bf[p][g][cc] =
+                *(const bf16x8_t*)(Bs + gu_swz(g * GBI + wn * 64 + cc * 32 + (lane & 31), ch));
+      };
+      read_frags(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int p = kk & 1;
+        if (kk + 1 < BK / 16) read_frags(kk + 1, p ^ 1);
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
           for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
-              acc[rr][g][cc] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[g][cc], acc[rr][g][cc], 0, 0, 0);
+              acc[rr][g][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][rr], bf[p][g][cc],
+                                                                       acc[rr][g][cc], 0, 0, 0);
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads of stage st + 1 landed
+      __syncthreads();  // every wave is done with buffer st & 1; stage st + 1 is visible
+      if (st + 2 < nst) load_stage(st + 2, st & 1);
     }
     // epilogue: lane holds column i = i0 + wn*64 + cc*32 + lane%32 for 16 rows of each row tile
     uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(PFT, 2) void ffn_prefill_gate_up_kernel(PfArgs a) {
         }
       }
     }
-    __syncthreads();  // s_w is rewritten by the next tile
+    __syncthreads();  // s_w and the LDS stages are rewritten by the next tile
   }
 }
 
@@ -385,7 +408,9 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_combine_kernel(PfArgs a) {
   a.y[(size_t)t * H + c] = f32_to_bf16_rne(s);
 }
 
-constexpr int kPfGrid = 512;  // persistent workgroups per GEMM launch (2 per CU: < 60 KiB LDS each)
+constexpr int kPfGrid = 512;  // persistent workgroups of the down GEMM (2 per CU: < 60 KiB LDS each)
+constexpr int kPfGridGu = 256;  // persistent workgroups of the gate/up GEMM (one per CU)
+constexpr size_t kPfGateUpLds = sizeof(uint16_t) * 2 * (size_t)GU_STAGE;
 
 // stage 0: gate/up; stage 1: down; stage 2: combine.  e0/e1 (nullable) time the launch.
 hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const void* arena,
@@ -394,8 +419,14 @@ hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const 
   PfArgs a{d, v, (const uint16_t*)x, (const unsigned char*)arena,
            (const unsigned char*)shared_blob, (uint16_t*)y, sel, group, ngroups, T,
            e0 != nullptr};
-  if (stage == 0)
-    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
+  if (stage == 0) {
+    const hipError_t e = hipFuncSetAttribute((const void*)ffn_prefill_gate_up_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kPfGateUpLds);
+    if (e != hipSuccess) return e;
+    return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGridGu), dim3(GU_T), kPfGateUpLds, s,
+                        e0, e1, a);
+  }
   if (stage == 1)
     return launch_timed(ffn_prefill_down_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
   return launch_timed(ffn_prefill_combine_kernel, dim3(T * (d.H / PFT)), dim3(PFT), 0, s, e0, e1,
