@@ -35,10 +35,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // register-frien
 constexpr int PFT = 256;        // threads (4 waves)
 constexpr int BM = 128;         // rows per tile
 constexpr int BK = 64;          // contraction per LDS stage (128-byte row segments)
-constexpr int LDK = BK + 8;     // padded LDS row (bf16): 144 bytes
 constexpr int GBI = 128;        // intermediate rows per gate/up tile (256 GEMM columns)
-constexpr int DBN = 128;        // output columns per down tile
-constexpr int DBM = 256;        // rows per down tile
 constexpr int kMaxEntriesPf = 1040;
 
 struct PfArgs {
@@ -139,22 +136,24 @@ __device__ __forceinline__ uint16_t pf_bf16(float f) { return f32_to_bf16_rne(f)
 // Tile = 256 rows x 128 intermediate rows (256 GEMM columns: 128 gate rows, then the 128 up
 // rows of the same i), one workgroup of eight waves per CU in a 4 x 2 arrangement; a wave owns
 // 64 rows x 64 i: eight 32 x 32 MFMA tiles (two row tiles times gate and up times two column
-// tiles) fed by six 16-byte LDS reads per 16-deep step, the next step's reads issued before
-// this step's MFMAs.  Operands go from global memory straight into LDS (gfx950's 16-byte
-// global-to-LDS loads: no registers, no LDS store instructions) in two stages of 64
-// contraction elements (32 KiB of rows + 32 KiB of weights each) with one barrier per stage:
-// a stage's loads are issued right after the barrier that frees its buffer and land while the
-// other stage computes.  Rows are 128 bytes without padding; 16-byte chunk c of row r sits at
-// chunk c ^ (r & 7), so the eight lanes an LDS read serves together (eight rows, one chunk)
-// fall on distinct banks.  Rows past the expert's count load a valid row: they only reach
-// output rows that are never stored.
+// tiles) fed by six 16-byte LDS reads per 16-deep step (written ahead of the previous step's
+// MFMAs; the compiler interleaves them).  Operands go from global memory straight into LDS
+// (gfx950's 16-byte global-to-LDS loads: no registers, no LDS store instructions) in two
+// stages of 64 contraction elements (32 KiB of rows + 32 KiB of weights each) with one barrier
+// per stage: a stage's loads are issued right after the barrier that frees its buffer and land
+// while the other stage computes.  Rows are 128 bytes without padding; 16-byte chunk c of row r
+// sits at chunk c ^ ((r / 2) % 8): gfx950's LDS serves a 16-byte read 16 lanes (256 bytes, all
+// 64 banks) at a time, and the 16 consecutive rows such a group reads at one chunk then fill
+// distinct 16-byte bank slots (row parity times the XOR).  Rows past the expert's count load a
+// valid row: they only reach output rows that are never stored.
 constexpr int GU_T = 512;                         // threads (8 waves)
 constexpr int GU_BM = 256;                        // rows per gate/up tile
 constexpr int GU_STAGE = (GU_BM + 2 * GBI) * BK;  // bf16 elements per LDS stage
 constexpr int GU_LPW = GU_STAGE * 2 / (16 * 64) / (GU_T / 64);  // 1 KiB loads per wave per stage (8)
 
+__device__ __forceinline__ int gu_sx(int row) { return (row >> 1) & 7; }  // chunk XOR of a row
 __device__ __forceinline__ int gu_swz(int row, int chunk) {  // element offset of (row, chunk)
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+  return row * BK + ((chunk ^ gu_sx(row)) << 3);
 }
 
 __global__ __launch_bounds__(GU_T, 1) void ffn_prefill_gate_up_kernel(PfArgs a) {
@@ -172,8 +171,8 @@ __global__ __launch_bounds__(GU_T, 1) void ffn_prefill_gate_up_kernel(PfArgs a) 
   const int nst = H / BK;  // contraction stages
   // global-to-LDS loads: load i of wave w fills LDS rows 8 (w * GU_LPW + i) .. + 7 of the
   // stage (rows 0..255: x rows, 256..511: weight rows); lane l brings row ... + l / 8,
-  // physical chunk l % 8 = logical chunk lc ^ (row & 7)
-  const int lrow = lane >> 3, lc = (lane & 7) ^ lrow;
+  // physical chunk l % 8, which holds logical chunk (l % 8) ^ gu_sx(row)
+  const int lrow = lane >> 3;
   for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
@@ -194,6 +193,7 @@ __global__ __launch_bounds__(GU_T, 1) void ffn_prefill_gate_up_kernel(PfArgs a) 
 #pragma unroll
     for (int i = 0; i < GU_LPW; ++i) {
       const int row = (wave * GU_LPW + i) * 8 + lrow;  // stage row 0 .. 511
+      const int lc = (lane & 7) ^ gu_sx(row);
       if (row < GU_BM) {
         const int r = m0 + row;
         const int tok = r >= en.rows ? (en.shared ? 0 : a.v.row_tok[en.row0]) :
@@ -280,111 +280,179 @@ __global__ __launch_bounds__(GU_T, 1) void ffn_prefill_gate_up_kernel(PfArgs a) 
 }
 
 // ---------------------------------------------------------------- down
-// Tile = 256 rows x 128 output columns; a wave owns 128 rows x 64 columns (eight 32 x 32 MFMA
-// tiles: six 16-byte LDS reads feed eight MFMAs), so every transposed WdT element in LDS
-// serves 256 rows.  Two workgroups (58 KiB LDS each) per CU.
-__global__ __launch_bounds__(PFT, 2) void ffn_prefill_down_kernel(PfArgs a) {
-  __shared__ __align__(16) uint16_t As[DBM * LDK];
-  __shared__ __align__(16) uint16_t Bs[DBN * LDK];  // [column][contraction]
+// Tile = 256 rows x 256 output columns, one workgroup of eight waves per CU in a 4 x 2
+// arrangement; a wave owns 64 rows x 128 columns (eight 32 x 32 MFMA tiles).  Both operands go
+// from global memory straight into LDS in two stages of 64 contraction elements: the a rows
+// (32 KiB, 128-byte rows, chunk c of row r at c ^ ((r / 2) % 8), as in gate/up) and 64 rows of the
+// stored transpose WdT as they lie in memory (32 KiB, [contraction][column], 512-byte rows).
+// The MFMA's B operand needs eight consecutive contraction values of one column per lane; the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16) gives four: within each group of 16 lanes,
+// lane j receives element j % 4 of the 8-byte reads of lanes 4m + j / 4 (m = 0..3), so lane
+// 4m + q of group g points at contraction row 8 (g / 2) + 4 h + m and columns
+// 16 (g % 2) + 4 q .. + 3 of a 32-column MFMA tile, and two reads (h = 0, 1) make a fragment.
+// One such read covers 4 contraction rows x 32 bytes per 16 lanes and 4 rows x 64 bytes per
+// 32 lanes; WdT's 16-byte chunk c of contraction row k sits at c ^ x(k % 4) with
+// x = {0, 6, 10, 12}, which puts both footprints on distinct banks.
+constexpr int DN_T = 512;   // threads (8 waves)
+constexpr int DN_BM = 256;  // rows per down tile
+constexpr int DN_BN = 256;  // output columns per down tile
+constexpr int DN_ASTAGE = DN_BM * BK;  // bf16 elements of a rows per stage
+constexpr int DN_STAGE = DN_ASTAGE + BK * DN_BN;
+constexpr int DN_ALPW = DN_ASTAGE * 2 / 1024 / (DN_T / 64);     // 1 KiB a loads per wave (4)
+constexpr int DN_BLPW = BK * DN_BN * 2 / 1024 / (DN_T / 64);    // 1 KiB WdT loads per wave (4)
+
+__device__ __forceinline__ int dn_bx(int k) {  // chunk XOR of WdT contraction row k
+  return (0xCA60 >> (4 * (k & 3))) & 15;         // nibbles 0, 6, 10, 12
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {  // byte address in LDS
+  return (uint32_t)(uintptr_t)(const lds_u16_t*)p;
+}
+
+// The eight transposing reads of one 16-deep step: two (byte offsets OFF and OFF + 2048, four
+// contraction rows apart) from each of this lane's four column-tile addresses, with the wait
+// for them in the same block.  Written as one asm block because the compiler's wait insertion
+// treats its transposing-read builtin as aliasing the global-to-LDS loads in flight and waits
+// for those first, which would serialise every stage's loads with its MFMAs; the stages are
+// ordered by the explicit wait and barrier at the end of each stage instead.
+template <int OFF>
+__device__ __forceinline__ void dn_read_b(s16x4_t (&r)[8], uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%c12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%c13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%c12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%c13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%c12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%c13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%c12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%c13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(OFF), "n"(OFF + 4 * DN_BN * 2)
+      : "memory");
+}
+
+__global__ __launch_bounds__(DN_T, 1) void ffn_prefill_down_kernel(PfArgs a) {
+  extern __shared__ __align__(16) uint16_t pf_smem[];  // 2 stages: a [rows][BK], WdT [BK][cols]
   __shared__ int s_mt[kMaxEntriesPf + 1];
   const Dims& d = a.d;
   const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int first;
-  const int n = pf_tile_prefix<DBM>(a, s_mt, first);
-  const int NT = H / DBN;
+  const int n = pf_tile_prefix<DN_BM>(a, s_mt, first);
+  const int NT = H / DN_BN;
   const int ntiles = s_mt[n] * NT;
-  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;     // A: rows lr + 32 h
-  // B: this thread's 4 consecutive contraction rows bk .. bk + 3, columns bc .. bc + 8, so the
-  // transpose into LDS is 8 stores of 4 contraction values (8 bytes) each.  The 16 lanes of a
-  // wave that share a column block take the 16 contraction offsets: one store instruction then
-  // covers every bank once per column block (with lanes on columns 8 apart, 8 * LDK bf16 is a
-  // multiple of the bank count and 16 lanes would hit one bank).
-  const int bk = (threadIdx.x & 15) * 4, bc = (threadIdx.x >> 4) * 8;
+  const int nst = I / BK;  // contraction stages (I is a multiple of 128)
+  // a loads: load i of wave w fills rows 8 (w * DN_ALPW + i) + lane / 8, physical chunk lane % 8
+  const int arow = lane >> 3;
+  // WdT loads: load i of wave w fills contraction rows 2 (w * DN_BLPW + i) + lane / 32, physical
+  // chunk lane % 32 (the row's parity is lane / 32; its residue mod 4 is set per load below)
+  const int brow = lane >> 5, bpc = lane & 31;
+  // transposing reads: this lane's contraction row and column within a 32 x 32 MFMA B tile
+  const int tg = lane >> 4, tm = (lane >> 2) & 3, tq = lane & 3;
+  const int tk = 8 * (tg >> 1) + tm;        // + 16 kk + 4 h: always tm modulo 4
+  const int tcol = 16 * (tg & 1) + 4 * tq;  // + 32 cc + 128 wn
+  int toff[4];  // element offset of this lane's read of column tile cc at kk = h = 0
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const int col = wn * 128 + cc * 32 + tcol;
+    toff[cc] = tk * DN_BN + (((col >> 3) ^ dn_bx(tm)) << 3) + (col & 7);
+  }
   for (int tile = xcd_order(); tile < ntiles; tile += gridDim.x) {
     const int mt = tile / NT, nt = tile - mt * NT;
     const int j = pf_find(s_mt, n, mt);
     const PfEntry en = pf_entry(a, first + j);
-    const int m0 = (mt - s_mt[j]) * DBM;
-    const int n0 = nt * DBN;
+    const int m0 = (mt - s_mt[j]) * DN_BM;
+    const int n0 = nt * DN_BN;
     const uint16_t* act = (en.shared ? a.v.pact_shared : a.v.pact) + (size_t)en.row0 * I;
-    // A rows: expert-sorted rows m0 + lr + 32 h; rows past the count read row 0 and are zeroed
-    int aoff[8];
-    unsigned amask = 0;  // bit h: row m0 + lr + 32 h exists
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const int r = m0 + lr + 32 * h;
-      const bool ok = r < en.rows;
-      amask |= ok ? 1u << h : 0u;
-      aoff[h] = (ok ? r : 0) * I;
-    }
     const uint16_t* wdt = (const uint16_t*)en.blob + (size_t)2 * I * H;  // WdT [I][H]
-    f32x16_t acc[4][2];
+    const uint16_t* asrc[DN_ALPW];
+    const uint16_t* bsrc[DN_BLPW];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
+    for (int i = 0; i < DN_ALPW; ++i) {
+      const int tr = (wave * DN_ALPW + i) * 8 + arow;  // tile row
+      const int r = m0 + tr;                             // rows past the count read row 0
+      asrc[i] = act + (size_t)(r < en.rows ? r : 0) * I + (((lane & 7) ^ gu_sx(tr)) << 3);
+    }
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+    for (int i = 0; i < DN_BLPW; ++i) {
+      const int k = (wave * DN_BLPW + i) * 2 + brow;  // contraction row within the stage
+      bsrc[i] = wdt + (size_t)k * H + n0 + ((bpc ^ dn_bx(k)) << 3);
+    }
+    f32x16_t acc[2][4];  // [row tile][column tile]
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[rr][cc][q] = 0.f;
-    u32x4_t ra[8], rb[4];
-    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+    auto load_stage = [&](int st, int buf) {
+      uint16_t* da = pf_smem + buf * DN_STAGE + wave * DN_ALPW * 8 * BK;
+      uint16_t* db = pf_smem + buf * DN_STAGE + DN_ASTAGE + wave * DN_BLPW * 2 * DN_BN;
+      const int k0 = st * BK;
 #pragma unroll
-    for (int h = 0; h < 8; ++h) ra[h] = *(const u32x4_t*)(act + aoff[h] + lc);
+      for (int i = 0; i < DN_ALPW; ++i)
+        __builtin_amdgcn_global_load_lds(asrc[i] + k0, da + i * 8 * BK, 16, 0, 0);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) rb[h] = *(const u32x4_t*)(wdt + (size_t)(bk + h) * H + n0 + bc);
-    for (int k0 = 0; k0 < I; k0 += BK) {
-      __syncthreads();
+      for (int i = 0; i < DN_BLPW; ++i)
+        __builtin_amdgcn_global_load_lds(bsrc[i] + (size_t)k0 * H, db + i * 2 * DN_BN, 16, 0, 0);
+    };
+    load_stage(0, 0);
+    load_stage(1, 1);  // I >= 128: at least 2 stages
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt <= 8: stage 0 has landed
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      const uint16_t* As = pf_smem + (st & 1) * DN_STAGE;
+      const uint32_t b0 = lds_addr(As + toff[0]), b1 = lds_addr(As + toff[1]);
+      const uint32_t b2 = lds_addr(As + toff[2]), b3 = lds_addr(As + toff[3]);
 #pragma unroll
-      for (int h = 0; h < 8; ++h)
-        *(u32x4_t*)(As + (lr + 32 * h) * LDK + lc) = (amask >> h) & 1u ? ra[h] : z4;
-      // transpose the 4 x 8 block: column c gets (row0, row1) and (row2, row3) packed pairs
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int ch = 2 * kk + (lane >> 5);
+        bf16x8_t af[2], bf[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t a0 = rb[0][q], a1 = rb[1][q], a2 = rb[2][q], a3 = rb[3][q];
-        const uint32_t lo01 = (a0 & 0xffffu) | (a1 << 16), hi01 = (a0 >> 16) | (a1 & 0xffff0000u);
-        const uint32_t lo23 = (a2 & 0xffffu) | (a3 << 16), hi23 = (a2 >> 16) | (a3 & 0xffff0000u);
-        *(uint2*)(Bs + (bc + 2 * q) * LDK + bk) = make_uint2(lo01, lo23);
-        *(uint2*)(Bs + (bc + 2 * q + 1) * LDK + bk) = make_uint2(hi01, hi23);
+        for (int rr = 0; rr < 2; ++rr)
+          af[rr] = *(const bf16x8_t*)(As + gu_swz(wm * 64 + rr * 32 + (lane & 31), ch));
+        s16x4_t h8[8];  // [cc][h]
+        constexpr int kBOff = DN_ASTAGE * 2;  // bytes from a stage's start to its WdT rows
+        if (kk == 0) dn_read_b<kBOff>(h8, b0, b1, b2, b3);
+        if (kk == 1) dn_read_b<kBOff + 16 * DN_BN * 2>(h8, b0, b1, b2, b3);
+        if (kk == 2) dn_read_b<kBOff + 32 * DN_BN * 2>(h8, b0, b1, b2, b3);
+        if (kk == 3) dn_read_b<kBOff + 48 * DN_BN * 2>(h8, b0, b1, b2, b3);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          bf[cc] = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(h8[2 * cc], h8[2 * cc + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+            acc[rr][cc] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[cc], acc[rr][cc], 0, 0, 0);
       }
-      __syncthreads();
-      const int kn = k0 + BK < I ? k0 + BK : k0;  // last stage: harmless reload
-#pragma unroll
-      for (int h = 0; h < 8; ++h) ra[h] = *(const u32x4_t*)(act + aoff[h] + kn + lc);
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        rb[h] = *(const u32x4_t*)(wdt + (size_t)(kn + bk + h) * H + n0 + bc);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += 16) {
-        const int ko = kk + 8 * (lane >> 5);
-        bf16x8_t af[4], bf[2];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          af[rr] = *(const bf16x8_t*)(As + (wm * 128 + rr * 32 + (lane & 31)) * LDK + ko);
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          bf[cc] = *(const bf16x8_t*)(Bs + (wn * 64 + cc * 32 + (lane & 31)) * LDK + ko);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-            acc[rr][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[rr], bf[cc], acc[rr][cc], 0, 0, 0);
-      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads of stage st + 1 landed
+      __syncthreads();  // every wave is done with buffer st & 1; stage st + 1 is visible
+      if (st + 2 < nst) load_stage(st + 2, st & 1);
     }
     float* yrow = en.shared ? a.v.pyexp_shared : a.v.pyexp;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
+    for (int rr = 0; rr < 2; ++rr) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int r = m0 + wm * 128 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int r = m0 + wm * 64 + rr * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
         if (r < en.rows) {
-          float* out = yrow + (size_t)(en.row0 + r) * H + n0 + wn * 64 + (lane & 31);
-          out[0] = acc[rr][0][q];
-          out[32] = acc[rr][1][q];
+          float* out = yrow + (size_t)(en.row0 + r) * H + n0 + wn * 128 + (lane & 31);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) out[32 * cc] = acc[rr][cc][q];
         }
       }
     }
+    __syncthreads();  // the LDS stages are rewritten by the next tile
   }
 }
 
@@ -408,7 +476,8 @@ __global__ __launch_bounds__(PFT) void ffn_prefill_combine_kernel(PfArgs a) {
   a.y[(size_t)t * H + c] = f32_to_bf16_rne(s);
 }
 
-constexpr int kPfGrid = 512;  // persistent workgroups of the down GEMM (2 per CU: < 60 KiB LDS each)
+constexpr int kPfGridDn = 256;  // persistent workgroups of the down GEMM (one per CU)
+constexpr size_t kPfDownLds = sizeof(uint16_t) * 2 * (size_t)DN_STAGE;
 constexpr int kPfGridGu = 256;  // persistent workgroups of the gate/up GEMM (one per CU)
 constexpr size_t kPfGateUpLds = sizeof(uint16_t) * 2 * (size_t)GU_STAGE;
 
@@ -427,14 +496,20 @@ hipError_t launch_ffn_prefill(const Dims& d, const Dev& v, const void* x, const 
     return launch_timed(ffn_prefill_gate_up_kernel, dim3(kPfGridGu), dim3(GU_T), kPfGateUpLds, s,
                         e0, e1, a);
   }
-  if (stage == 1)
-    return launch_timed(ffn_prefill_down_kernel, dim3(kPfGrid), dim3(PFT), 0, s, e0, e1, a);
+  if (stage == 1) {
+    const hipError_t e = hipFuncSetAttribute((const void*)ffn_prefill_down_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kPfDownLds);
+    if (e != hipSuccess) return e;
+    return launch_timed(ffn_prefill_down_kernel, dim3(kPfGridDn), dim3(DN_T), kPfDownLds, s, e0,
+                        e1, a);
+  }
   return launch_timed(ffn_prefill_combine_kernel, dim3(T * (d.H / PFT)), dim3(PFT), 0, s, e0, e1,
                       a);
 }
 
 bool prefill_ffn_supported(const Dims& d) {
-  return d.fmt == FMT_BF16 && d.I % GBI == 0 && d.H % DBN == 0 && d.K <= 16 &&
+  return d.fmt == FMT_BF16 && d.I % GBI == 0 && d.H % DN_BN == 0 && d.K <= 16 &&
          d.umax + d.has_shared <= kMaxEntriesPf;
 }
 
