@@ -278,6 +278,11 @@ __device__ __forceinline__ float gu_chunk_scale(const unsigned char* blob, int H
 
 // Butterfly reduce-scatter over the wave of M = 2 * NTOK units (gate, up): afterwards lane l
 // holds the wave total of unit gu_unit<NTOK>(l) (every lane sharing that unit holds it).
+// Read-only views of plan arrays for uniform indices: loads through the constant address
+// space become scalar loads (the arrays are written by an earlier launch, never by this one).
+typedef __attribute__((address_space(4))) const int kconst_i32;
+typedef __attribute__((address_space(4))) const float kconst_f32;
+
 template <int NTOK>
 __device__ __forceinline__ void wave_reduce_units(float* gv, float* uv, int lane) {
 #pragma unroll
@@ -351,15 +356,30 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
     atomicAdd(&a.v.stats[STAT_FFN_BYTES], (unsigned long long)d.S);
     if (a.timed) atomicAdd(&a.v.stats[STAT_TIMED_BLOB_BYTES], (unsigned long long)d.S);
   }
-  // routed tokens and their weights first: they are the only loads the activations wait on
+  // routed tokens and their weights: scalar loads issued together behind the first pass's
+  // weight stream (the plan wrote them before this launch; per-token vector loads each waited
+  // before the next, and in front of the weight loads); the staged activations' addresses then
+  // wait on them alone.  For the shared expert (row0 0) the loaded values are valid, unused.
   int tok[NTOK];
   float wt[NTOK];
+  auto load_tokens = [&]() {
+    const kconst_i32* rt = (const kconst_i32*)(a.v.row_tok + en.row0);
+    const kconst_f32* rw = (const kconst_f32*)(a.v.row_w + en.row0);
+    int lt[NTOK];
+    float lw[NTOK];
 #pragma unroll
-  for (int t = 0; t < NTOK; ++t) {
-    const int tc = t < ntok ? t : 0;
-    tok[t] = en.shared ? tc : a.v.row_tok[en.row0 + tc];
-    wt[t] = en.shared ? 1.0f : a.v.row_w[en.row0 + tc];
-  }
+    for (int t = 0; t < NTOK; ++t) {
+      const int tc = t < ntok ? t : 0;
+      lt[t] = rt[tc];
+      lw[t] = rw[tc];
+    }
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) {
+      const int tc = t < ntok ? t : 0;
+      tok[t] = en.shared ? tc : lt[t];
+      wt[t] = en.shared ? 1.0f : lw[t];
+    }
+  };
   const int i0 = rb * RA + wave, i1 = i0 + 4;
   const size_t rbytes = F::row_bytes(2 * H), hbytes = F::row_bytes(H);
   const unsigned char* r0 = en.blob + (size_t)i0 * rbytes;
@@ -374,24 +394,6 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
     u32x4v wg0[GN], wu0[GN], wg1[GN], wu1[GN];
     float sg0[GN], su0[GN], sg1[GN], su1[GN];  // block scales (fp8, MXFP4)
     u32x4v sv[NSV];
-    if constexpr (NTOK > 1) {
-      // the pass's activations of every routed token, staged in LDS as [t][GN * 64 chunks of
-      // EPL] (rows past the entry's tokens repeat its first token): their loads go out first,
-      // then the weight stream, so the LDS stores wait for the activations alone
-      lds_barrier();  // the previous pass is done with s_x
-#pragma unroll
-      for (int q = 0; q < NSV; ++q) {
-        const int idx = (int)threadIdx.x + q * FT;
-        const int t = idx / (PC * XV), r = idx % (PC * XV);
-        const int c = kb * 64 + r / XV;
-        const int cc = c < ngq ? c : ngq - 1;
-        const int tt = t < ntok ? t : 0;
-        int tk = tok[0];
-#pragma unroll
-        for (int q2 = 1; q2 < NTOK; ++q2) tk = tt == q2 ? tok[q2] : tk;
-        sv[q] = *(const u32x4v*)(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8);
-      }
-    }
 #pragma unroll
     for (int k = 0; k < GN; ++k) {
       int c = (kb + k) * 64 + lane;
@@ -410,6 +412,24 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
         su0[k] = gu_chunk_scale<FMT>(en.blob, H, I, i0, 1, c);
         sg1[k] = gu_chunk_scale<FMT>(en.blob, H, I, i1, 0, c);
         su1[k] = gu_chunk_scale<FMT>(en.blob, H, I, i1, 1, c);
+      }
+    }
+    if (kb == 0) load_tokens();
+    if constexpr (NTOK > 1) {
+      // the pass's activations of every routed token, staged in LDS as [t][GN * 64 chunks of
+      // EPL] (rows past the entry's tokens repeat its first token), behind the weight stream
+      lds_barrier();  // the previous pass is done with s_x
+#pragma unroll
+      for (int q = 0; q < NSV; ++q) {
+        const int idx = (int)threadIdx.x + q * FT;
+        const int t = idx / (PC * XV), r = idx % (PC * XV);
+        const int c = kb * 64 + r / XV;
+        const int cc = c < ngq ? c : ngq - 1;
+        const int tt = t < ntok ? t : 0;
+        int tk = tok[0];
+#pragma unroll
+        for (int q2 = 1; q2 < NTOK; ++q2) tk = tt == q2 ? tok[q2] : tk;
+        sv[q] = *(const u32x4v*)(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8);
       }
     }
     if constexpr (NTOK == 1) {
