@@ -320,19 +320,22 @@ __device__ __forceinline__ int gu_unit(int lane) {
 }
 
 template <int FMT>
-struct GuX {  // 16-byte activation vectors per weight chunk
-  static constexpr int XV = Fmt<FMT>::EPL / 8;
+struct GuX {
+  static constexpr int XV = Fmt<FMT>::EPL / 8;  // 16-byte activation vectors per weight chunk
+  // gate chunk groups of 64 per lane per pass: three for e2m1 (a 6144-wide row is 192 chunks
+  // of 32 codes, so a fourth group would only reload the last chunk), else GN
+  static constexpr int GNF = FMT == FMT_MXFP4 ? 3 : GN;
 };
 
 // At one token: the lane's activations of pass kb (gate chunks c = (kb + k) * 64 + lane).
 // xrow: the token's activation row ([H] bf16).
 template <int FMT>
 __device__ __forceinline__ void load_x1(const FfnArgs& a, int kb, int lane,
-                                        u32x4v (&xr)[GN][GuX<FMT>::XV], const uint16_t* xrow) {
+                                        u32x4v (&xr)[GuX<FMT>::GNF][GuX<FMT>::XV], const uint16_t* xrow) {
   constexpr int EPL = Fmt<FMT>::EPL, XV = GuX<FMT>::XV;
   const int ngq = a.d.H / EPL;
 #pragma unroll
-  for (int k = 0; k < GN; ++k) {
+  for (int k = 0; k < GuX<FMT>::GNF; ++k) {
     int c = (kb + k) * 64 + lane;
     c = c < ngq ? c : ngq - 1;
     const u32x4v* p = (const u32x4v*)(xrow + (size_t)c * EPL);
@@ -341,13 +344,23 @@ __device__ __forceinline__ void load_x1(const FfnArgs& a, int kb, int lane,
   }
 }
 
+// Chunks per token of the staged activations of a gate/up pass at more than one token: a
+// pass covers GNF * 64 chunks, trimmed for rows shorter than that to the staging loads' own
+// granularity (FT / XV chunks), so no LDS is reserved for chunks that are never loaded.
+template <int FMT>
+__host__ __device__ inline int gate_up_stage_chunks(int ngq) {
+  constexpr int CPI = FT / GuX<FMT>::XV, PC = GuX<FMT>::GNF * 64;
+  const int rounded = (ngq + CPI - 1) / CPI * CPI;
+  return rounded < PC ? rounded : PC;
+}
+
 // xrow (NTOK == 1): the activation row of the entry's one token, for passes after the first.
 template <int FMT, int NTOK>
 __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
-                             u32x4v (&xr)[GN][GuX<FMT>::XV], uint16_t* s_x,
+                             u32x4v (&xr)[GuX<FMT>::GNF][GuX<FMT>::XV], uint16_t* s_x,
                              const uint16_t* xrow) {
   using F = Fmt<FMT>;
-  constexpr int EPL = F::EPL, XV = GuX<FMT>::XV;
+  constexpr int EPL = F::EPL, XV = GuX<FMT>::XV, GN = GuX<FMT>::GNF;
   const Dims& d = a.d;
   const int H = d.H, I = d.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -389,11 +402,11 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) g0[t] = u0[t] = g1[t] = u1[t] = 0.f;
   constexpr int PC = GN * 64;                           // chunk slots per token per pass
-  constexpr int NSV = NTOK > 1 ? NTOK * PC * GuX<FMT>::XV / FT : 1;  // staged vectors/thread
+  constexpr int CPI = FT / XV;  // chunks one staging load of the workgroup covers
+  const int pce = gate_up_stage_chunks<FMT>(ngq);  // staged chunks per token
   for (int kb = 0; kb * 64 < ngq; kb += GN) {
     u32x4v wg0[GN], wu0[GN], wg1[GN], wu1[GN];
     float sg0[GN], su0[GN], sg1[GN], su1[GN];  // block scales (fp8, MXFP4)
-    u32x4v sv[NSV];
 #pragma unroll
     for (int k = 0; k < GN; ++k) {
       int c = (kb + k) * 64 + lane;
@@ -416,29 +429,31 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
     }
     if (kb == 0) load_tokens();
     if constexpr (NTOK > 1) {
-      // the pass's activations of every routed token, staged in LDS as [t][GN * 64 chunks of
-      // EPL] (rows past the entry's tokens repeat its first token), behind the weight stream
-      lds_barrier();  // the previous pass is done with s_x
+      // the pass's activations of every routed token, staged in LDS as [t][pce chunks of EPL]
+      // (rows past the entry's tokens repeat its first token) by 16-byte global-to-LDS loads
+      // behind the weight stream: no registers held for them.  Load q2 of token t covers the
+      // pass's chunks q2 * CPI .. + CPI - 1; loads wholly past the row are skipped, and lanes
+      // past it load its last chunk into slots no product reads.
+      if (kb > 0) lds_barrier();  // the previous pass is done with s_x
 #pragma unroll
-      for (int q = 0; q < NSV; ++q) {
-        const int idx = (int)threadIdx.x + q * FT;
-        const int t = idx / (PC * XV), r = idx % (PC * XV);
-        const int c = kb * 64 + r / XV;
-        const int cc = c < ngq ? c : ngq - 1;
-        const int tt = t < ntok ? t : 0;
-        int tk = tok[0];
+      for (int t = 0; t < NTOK; ++t) {
+        const int tk = tok[t < ntok ? t : 0];
 #pragma unroll
-        for (int q2 = 1; q2 < NTOK; ++q2) tk = tt == q2 ? tok[q2] : tk;
-        sv[q] = *(const u32x4v*)(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8);
+        for (int q2 = 0; q2 < XV; ++q2) {
+          if (kb * 64 + q2 * CPI >= ngq) continue;  // uniform
+          const int r = q2 * FT + (int)threadIdx.x;
+          const int c = kb * 64 + r / XV;
+          const int cc = c < ngq ? c : ngq - 1;
+          __builtin_amdgcn_global_load_lds(a.x + (size_t)tk * H + (size_t)cc * EPL + (r % XV) * 8,
+                                           s_x + ((size_t)t * pce * XV + q2 * FT + wave * 64) * 8,
+                                           16, 0, 0);
+        }
       }
     }
     if constexpr (NTOK == 1) {
       if (kb > 0) load_x1<FMT>(a, kb, lane, xr, xrow);
     } else {
-#pragma unroll
-      for (int q = 0; q < NSV; ++q)
-        *(u32x4v*)(s_x + ((size_t)threadIdx.x + (size_t)q * FT) * 8) = sv[q];
-      lds_barrier();
+      lds_barrier();  // waits for the staging loads (and the weight loads issued before them)
     }
 #pragma unroll
     for (int k = 0; k < GN; ++k) {
@@ -462,7 +477,7 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
               }
             } else {
               const u32x4v* sp =
-                  (const u32x4v*)(s_x + ((size_t)t * GN * 64 * XV + (size_t)(k * 64 + lane) * XV) * 8);
+                  (const u32x4v*)(s_x + ((size_t)t * pce * XV + (size_t)(k * 64 + lane) * XV) * 8);
 #pragma unroll
               for (int q = 0; q < XV; ++q) {
                 const u32x4v v = sp[q];
@@ -900,7 +915,7 @@ template <int FMT, int NTOK>
 __global__ __launch_bounds__(FT) void ffn_gate_up_kernel(FfnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int nra = a.d.I / RA;
-  u32x4v xr[GN][GuX<FMT>::XV];
+  u32x4v xr[GuX<FMT>::GNF][GuX<FMT>::XV];
   if constexpr (NTOK == 1) {
     // at one token the activations do not depend on the plan: they go out before the entry
     load_x1<FMT>(a, 0, threadIdx.x & 63, xr, a.x);
@@ -925,8 +940,10 @@ __global__ __launch_bounds__(FT) void ffn_gate_up_kernel(FfnArgs a) {
 }
 
 template <int FMT, int NTOK>
-static size_t gate_up_lds_bytes() {
-  return NTOK > 1 ? (size_t)NTOK * GN * 64 * Fmt<FMT>::EPL * 2 : 0;
+static size_t gate_up_lds_bytes(const Dims& d) {
+  return NTOK > 1 ? (size_t)NTOK * gate_up_stage_chunks<FMT>(d.H / Fmt<FMT>::EPL) *
+                        Fmt<FMT>::EPL * 2
+                  : 0;
 }
 
 template <int FMT, int NTOK>
@@ -1026,7 +1043,7 @@ static hipError_t launch_ffn(const FfnArgs& a, int stage, hipStream_t s, hipEven
   constexpr int HC = down_hc<FMT>();
   if (stage == 0)
     return launch_with_lds(ffn_gate_up_kernel<FMT, NTOK>, a.NE * (d.I / RA),
-                           gate_up_lds_bytes<FMT, NTOK>(), a, s, e0, e1);
+                           gate_up_lds_bytes<FMT, NTOK>(d), a, s, e0, e1);
   const size_t dlds =
       sizeof(float) * ((size_t)4 * NTOK * HC + (NTOK > 1 ? (size_t)NTOK * (d.I / d.RS) : 0));
   hipError_t e = launch_with_lds(ffn_down_kernel<FMT, NTOK>, a.NE * (d.H / HC) * d.RS, dlds, a,
