@@ -432,15 +432,17 @@ __device__ void gate_up_role(const FfnArgs& a, const Entry& en, int rb,
       // the pass's activations of every routed token, staged in LDS as [t][pce chunks of EPL]
       // (rows past the entry's tokens repeat its first token) by 16-byte global-to-LDS loads
       // behind the weight stream: no registers held for them.  Load q2 of token t covers the
-      // pass's chunks q2 * CPI .. + CPI - 1; loads wholly past the row are skipped, and lanes
-      // past it load its last chunk into slots no product reads.
+      // pass's chunks q2 * CPI .. + CPI - 1; loads outside the pass or wholly past the row are
+      // skipped, and lanes past the row load its last chunk into slots no product reads.
       if (kb > 0) lds_barrier();  // the previous pass is done with s_x
 #pragma unroll
       for (int t = 0; t < NTOK; ++t) {
         const int tk = tok[t < ntok ? t : 0];
 #pragma unroll
         for (int q2 = 0; q2 < XV; ++q2) {
-          if (kb * 64 + q2 * CPI >= ngq) continue;  // uniform
+          // uniform: outside the pass (an e2m1 pass is 3 of the 4 groups a token's XV loads
+          // could cover) or wholly past the row
+          if (q2 * CPI >= PC || kb * 64 + q2 * CPI >= ngq) continue;
           const int r = q2 * FT + (int)threadIdx.x;
           const int c = kb * 64 + r / XV;
           const int cc = c < ngq ? c : ngq - 1;

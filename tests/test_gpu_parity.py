@@ -128,6 +128,26 @@ def test_fp8_decode_with_shared_expert(groups):
     _log(f"fp8: max rel-L2 {max(errs):.2e}")
 
 
+@pytest.mark.parametrize("fmt,hidden,tokens,shared", [
+    (2, 8192, 4, False),   # e2m1: 256 chunks per half-row in passes of 192, the second partial
+    (2, 8192, 1, False),   # e2m1 at one token: activations in registers, the same passes
+    (1, 6144, 2, True),    # fp8: 384 chunks in passes of 256, the second partial; shared expert
+    (0, 3072, 4, False),   # bf16: 384 chunks in passes of 256, staged activations
+])
+def test_decode_rows_longer_than_one_pass(fmt, hidden, tokens, shared):
+    """Decode steps whose gate/up rows take more than one pass of the weight stream (the last
+    pass partial), at one and at several tokens, for each weight format; 16 experts top-8, so
+    the step's tokens share experts and their activations are staged in LDS."""
+    base = mi.WORKLOADS["qwen35b_decode"]
+    wl = dataclasses.replace(base, name=f"passes_f{fmt}_h{hidden}_t{tokens}", layers=2,
+                             hidden=hidden, inter=256, experts=16, fmt=fmt, cache_frac=0.75,
+                             tokens_per_step=tokens, token_steps=8, has_shared=shared)
+    _log(f"case {wl.name} C={wl.capacity}")
+    with _bench(wl, groups=0) as wb:
+        errs = run_parity(wb, wl.token_steps)
+    _log(f"{wl.name}: max rel-L2 {max(errs):.2e}")
+
+
 @pytest.mark.parametrize("groups", [0, 2])
 def test_mxfp4_four_streams_with_resize(groups):
     """753B-like shape: H 6144, 256 experts top-8, MXFP4, 4 streams per step with cross-request
