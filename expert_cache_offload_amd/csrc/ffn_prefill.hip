@@ -13,12 +13,13 @@
 //              gate rows and the 128 up rows, so each wave holds gate and up of the same
 //              (row, i) in the same lane and the epilogue a = silu(g) * u * w is per lane;
 //              eight waves, each 64 rows x 64 intermediate rows (eight 32 x 32 MFMA tiles:
-//              six 16-byte LDS reads feed eight MFMAs); operands land in LDS by direct
-//              global-to-LDS loads; rows are gathered from x by the plan's row -> token map;
-//              a is stored bf16;
-//   down     - tile = 256 rows x 128 output columns over the stored transpose WdT, whose
-//              rows are contraction rows: the B tile is transposed on its way into LDS;
-//              fp32 partial rows per (token, choice); four waves, 128 x 64 each;
+//              six 16-byte LDS reads feed eight MFMAs, the next step's reads issued in the
+//              same asm block as this step's MFMAs); rows are gathered from x by the plan's
+//              row -> token map; a is stored bf16;
+//   down     - tile = 256 rows x 256 output columns over the stored transpose WdT
+//              ([contraction][column]), loaded into LDS as stored and read with gfx950's
+//              transposing LDS reads; eight waves, 64 x 128 each; fp32 partial rows per
+//              (token, choice);
 //   combine  - y[t] = bf16(sum over the token's k rows (+ shared) in a fixed order).
 // A 64-wide contraction stage in LDS with the next stage's global loads in flight during the
 // MFMAs.  Workgroups are persistent over the launch's tiles, whose count depends on the plan
@@ -132,6 +133,70 @@ __device__ __forceinline__ int xcd_order() {
 
 __device__ __forceinline__ uint16_t pf_bf16(float f) { return f32_to_bf16_rne(f); }
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {  // byte address in LDS
+  return (uint32_t)(uintptr_t)(const lds_u16_t*)p;
+}
+
+// One 16-deep step of the gate/up tile in one asm block: the next step's six fragment reads
+// (two row tiles of x at byte offsets 0 and 4096 from `aa`; gate and up of two column tiles at
+// 0, 4096, 16384 and 20480 from `ba`) go out first, then this step's eight MFMAs
+// (c[rr * 4 + g * 2 + cc] += a[rr] x b[g * 2 + cc]), and the block ends waiting for its reads,
+// which land under the MFMAs.  Written as asm because the compiler, with global-to-LDS loads in
+// the kernel, waits for every outstanding LDS read before each MFMA group.  The block's MFMAs
+// are invisible to the compiler's hazard tracking: their accumulators are read by compiled
+// code only after gu_drain().
+__device__ __forceinline__ void gu_step(f32x16_t& c0, f32x16_t& c1, f32x16_t& c2, f32x16_t& c3,
+                                        f32x16_t& c4, f32x16_t& c5, f32x16_t& c6, f32x16_t& c7,
+                                        const bf16x8_t (&a)[2], const bf16x8_t (&b)[4],
+                                        bf16x8_t (&na)[2], bf16x8_t (&nb)[4], uint32_t aa,
+                                        uint32_t ba) {
+  asm volatile(
+      "ds_read_b128 %0, %20\n\t"
+      "ds_read_b128 %1, %20 offset:4096\n\t"
+      "ds_read_b128 %2, %21\n\t"
+      "ds_read_b128 %3, %21 offset:4096\n\t"
+      "ds_read_b128 %4, %21 offset:16384\n\t"
+      "ds_read_b128 %5, %21 offset:20480\n\t"
+      "v_mfma_f32_32x32x16_bf16 %6, %14, %16, %6\n\t"
+      "v_mfma_f32_32x32x16_bf16 %7, %14, %17, %7\n\t"
+      "v_mfma_f32_32x32x16_bf16 %8, %14, %18, %8\n\t"
+      "v_mfma_f32_32x32x16_bf16 %9, %14, %19, %9\n\t"
+      "v_mfma_f32_32x32x16_bf16 %10, %15, %16, %10\n\t"
+      "v_mfma_f32_32x32x16_bf16 %11, %15, %17, %11\n\t"
+      "v_mfma_f32_32x32x16_bf16 %12, %15, %18, %12\n\t"
+      "v_mfma_f32_32x32x16_bf16 %13, %15, %19, %13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(na[0]), "=&v"(na[1]), "=&v"(nb[0]), "=&v"(nb[1]), "=&v"(nb[2]), "=&v"(nb[3]),
+        "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7)
+      : "v"(a[0]), "v"(a[1]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(aa), "v"(ba)
+      : "memory");
+}
+
+// The last step of a stage: its eight MFMAs only.
+__device__ __forceinline__ void gu_step_last(f32x16_t& c0, f32x16_t& c1, f32x16_t& c2,
+                                             f32x16_t& c3, f32x16_t& c4, f32x16_t& c5,
+                                             f32x16_t& c6, f32x16_t& c7, const bf16x8_t (&a)[2],
+                                             const bf16x8_t (&b)[4]) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %10, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %8, %11, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %12, %2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %8, %13, %3\n\t"
+      "v_mfma_f32_32x32x16_bf16 %4, %9, %10, %4\n\t"
+      "v_mfma_f32_32x32x16_bf16 %5, %9, %11, %5\n\t"
+      "v_mfma_f32_32x32x16_bf16 %6, %9, %12, %6\n\t"
+      "v_mfma_f32_32x32x16_bf16 %7, %9, %13, %7"
+      : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7)
+      : "v"(a[0]), "v"(a[1]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3])
+      : "memory");
+}
+
+// Wait states after asm MFMAs before compiled code reads their results (the 16-pass
+// 32 x 32 MFMA needs up to 18 before a VALU read of its destination).
+__device__ __forceinline__ void gu_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // ---------------------------------------------------------------- gate / up
 // Tile = 256 rows x 128 intermediate rows (256 GEMM columns: 128 gate rows, then the 128 up
 // rows of the same i), one workgroup of eight waves per CU in a 4 x 2 arrangement; a wave owns
@@ -227,37 +292,42 @@ __global__ __launch_bounds__(GU_T, 1) void ffn_prefill_gate_up_kernel(PfArgs a) 
     for (int st = 0; st < nst; ++st) {
       const uint16_t* As = pf_smem + (st & 1) * GU_STAGE;
       const uint16_t* Bs = As + GU_BM * BK;
-      bf16x8_t af[2][2], bf[2][2][2];  // [step parity][...]
-      auto read_frags = [&](int kk, int p) {
-        const int ch = 2 * kk + (lane >> 5);  // 16-byte chunk of this lane's operands
+      // this lane's fragment addresses of step kk: x rows wm * 64 + (lane % 32) (+ 32 for the
+      // second row tile) and weight rows wn * 64 + (lane % 32) (+ 32 per column tile, + GBI
+      // for up), all at the lane's 16-byte chunk 2 kk + lane / 32
+      auto aaddr = [&](int kk) {
+        return lds_addr(As + gu_swz(wm * 64 + (lane & 31), 2 * kk + (lane >> 5)));
+      };
+      auto baddr = [&](int kk) {
+        return lds_addr(Bs + gu_swz(wn * 64 + (lane & 31), 2 * kk + (lane >> 5)));
+      };
+      bf16x8_t f0a[2], f0b[4], f1a[2], f1b[4];
+      {  // step 0: plain loads (the compiler waits for them before the first block)
+        const int ch = lane >> 5;
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
-          af[p][rr] = *(const bf16x8_t*)(As + gu_swz(wm * 64 + rr * 32 + (lane & 31), ch));
+          f0a[rr] = *(const bf16x8_t*)(As + gu_swz(wm * 64 + rr * 32 + (lane & 31), ch));
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc)
-            bf[p][g][cc] =
+            f0b[g * 2 + cc] =
                 *(const bf16x8_t*)(Bs + gu_swz(g * GBI + wn * 64 + cc * 32 + (lane & 31), ch));
-      };
-      read_frags(0, 0);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int p = kk & 1;
-        if (kk + 1 < BK / 16) read_frags(kk + 1, p ^ 1);
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
-              acc[rr][g][cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][rr], bf[p][g][cc],
-                                                                       acc[rr][g][cc], 0, 0, 0);
       }
+      static_assert(BK / 16 == 4, "four steps per stage");
+      gu_step(acc[0][0][0], acc[0][0][1], acc[0][1][0], acc[0][1][1], acc[1][0][0], acc[1][0][1],
+              acc[1][1][0], acc[1][1][1], f0a, f0b, f1a, f1b, aaddr(1), baddr(1));
+      gu_step(acc[0][0][0], acc[0][0][1], acc[0][1][0], acc[0][1][1], acc[1][0][0], acc[1][0][1],
+              acc[1][1][0], acc[1][1][1], f1a, f1b, f0a, f0b, aaddr(2), baddr(2));
+      gu_step(acc[0][0][0], acc[0][0][1], acc[0][1][0], acc[0][1][1], acc[1][0][0], acc[1][0][1],
+              acc[1][1][0], acc[1][1][1], f0a, f0b, f1a, f1b, aaddr(3), baddr(3));
+      gu_step_last(acc[0][0][0], acc[0][0][1], acc[0][1][0], acc[0][1][1], acc[1][0][0],
+                   acc[1][0][1], acc[1][1][0], acc[1][1][1], f1a, f1b);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0: this wave's loads of stage st + 1 landed
       __syncthreads();  // every wave is done with buffer st & 1; stage st + 1 is visible
       if (st + 2 < nst) load_stage(st + 2, st & 1);
     }
+    gu_drain();
     // epilogue: lane holds column i = i0 + wn*64 + cc*32 + lane%32 for 16 rows of each row tile
     uint16_t* act = en.shared ? a.v.pact_shared : a.v.pact;
 #pragma unroll
@@ -306,12 +376,6 @@ __device__ __forceinline__ int dn_bx(int k) {  // chunk XOR of WdT contraction r
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {  // byte address in LDS
-  return (uint32_t)(uintptr_t)(const lds_u16_t*)p;
-}
-
 // The eight transposing reads of one 16-deep step: two (byte offsets OFF and OFF + 2048, four
 // contraction rows apart) from each of this lane's four column-tile addresses, with the wait
 // for them in the same block.  Written as one asm block because the compiler's wait insertion
