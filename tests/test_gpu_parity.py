@@ -133,11 +133,14 @@ def test_fp8_decode_with_shared_expert(groups):
     (2, 8192, 1, False),   # e2m1 at one token: activations in registers, the same passes
     (1, 6144, 2, True),    # fp8: 384 chunks in passes of 256, the second partial; shared expert
     (0, 3072, 4, False),   # bf16: 384 chunks in passes of 256, staged activations
+    (0, 2048, 3, False),   # bf16, 3 tokens: kernels built for 4, the fourth masked
+    (2, 6144, 6, False),   # e2m1, 6 tokens: kernels built for 8, two masked
 ])
 def test_decode_rows_longer_than_one_pass(fmt, hidden, tokens, shared):
     """Decode steps whose gate/up rows take more than one pass of the weight stream (the last
-    pass partial), at one and at several tokens, for each weight format; 16 experts top-8, so
-    the step's tokens share experts and their activations are staged in LDS."""
+    pass partial), at one and at several tokens, for each weight format, and token counts
+    between the kernels' bounds (1, 2, 4, 8); 16 experts top-8, so the step's tokens share
+    experts and their activations are staged in LDS."""
     base = mi.WORKLOADS["qwen35b_decode"]
     wl = dataclasses.replace(base, name=f"passes_f{fmt}_h{hidden}_t{tokens}", layers=2,
                              hidden=hidden, inter=256, experts=16, fmt=fmt, cache_frac=0.75,
