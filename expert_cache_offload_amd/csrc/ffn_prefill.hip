@@ -31,10 +31,8 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // register-friendly 16 bytes
 
-constexpr int PFT = 256;        // threads (4 waves)
-constexpr int BM = 128;         // rows per tile
+constexpr int PFT = 256;        // threads of the combine kernel
 constexpr int BK = 64;          // contraction per LDS stage (128-byte row segments)
 constexpr int GBI = 128;        // intermediate rows per gate/up tile (256 GEMM columns)
 constexpr int kMaxEntriesPf = 1040;
