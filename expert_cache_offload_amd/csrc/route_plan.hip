@@ -146,31 +146,85 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
   plan_begin_store(d, s, ps);
   __syncthreads();
 
-  // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
-  // the experts of rank < K are the selection, in order.  P adjacent lanes count one
-  // (token, expert) pair, each over 1/P of the experts, and add their counts (P = 2 measured
-  // best at E = 128: one pair per thread of the workgroup at one token).
-  {
-    constexpr int P = 2;
-    const int part = (E + P - 1) / P;
-    for (int idx = threadIdx.x; idx < P * T * E; idx += RT) {
-      const int i = idx / P, h = idx % P;
-      const int t = i / E, e = i - t * E;
-      const double z = s_z[i];
-      const double* zt = s_z + (size_t)t * E;
-      const int e_beg = h * part, e_end = e_beg + part < E ? e_beg + part : E;
-      int rank = 0;
+  // Top-k per token, ties to the lower expert id.  Counting ranks costs T * E^2 / RT compares
+  // per thread; the wave argmax costs K rounds of a six-step shuffle chain per token a wave
+  // holds.  Measured crossover: counting ranks is faster up to about T * E^2 = 8192 * K * (tokens
+  // per wave) (one token of 128 or 256 experts: 16.7 / 24.4 against 23.4 / 25.6 us per launch),
+  // the argmax beyond (four tokens of 256 experts: 42.6 against 64.5 us).
+  if ((long long)T * E * E <= 8192ll * K * ((T + 3) / 4)) {
+    // top-k per token by rank: rank(e) = #{e' : z_e' > z_e or (z_e' == z_e and e' < e)};
+    // the experts of rank < K are the selection, in order.  P adjacent lanes count one
+    // (token, expert) pair, each over 1/P of the experts, and add their counts (P = 2 measured
+    // best at E = 128: one pair per thread of the workgroup at one token).
+    {
+      constexpr int P = 2;
+      const int part = (E + P - 1) / P;
+      for (int idx = threadIdx.x; idx < P * T * E; idx += RT) {
+        const int i = idx / P, h = idx % P;
+        const int t = i / E, e = i - t * E;
+        const double z = s_z[i];
+        const double* zt = s_z + (size_t)t * E;
+        const int e_beg = h * part, e_end = e_beg + part < E ? e_beg + part : E;
+        int rank = 0;
 #pragma unroll 8
-      for (int e2 = e_beg; e2 < e_end; ++e2) {  // 8 LDS reads in flight per step
-        const double z2 = zt[e2];
-        rank += (z2 > z) || (z2 == z && e2 < e);
-      }
+        for (int e2 = e_beg; e2 < e_end; ++e2) {  // 8 LDS reads in flight per step
+          const double z2 = zt[e2];
+          rank += (z2 > z) || (z2 == z && e2 < e);
+        }
 #pragma unroll
-      for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);  // the P lanes are adjacent
-                                                                     // and all active
-      if (h == 0 && rank < K) {
-        s_tk_idx[t * K + rank] = e;
-        s_tk_z[t * K + rank] = z;
+        for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o);  // the P lanes are adjacent
+                                                                       // and all active
+        if (h == 0 && rank < K) {
+          s_tk_idx[t * K + rank] = e;
+          s_tk_z[t * K + rank] = z;
+        }
+      }
+    }
+  } else {
+    // one wave per token (tokens w, w + 4): K rounds of a wave-wide argmax over the token's
+    // logits held in registers (lane l holds experts l, l + 64, ...), largest logit first, ties
+    // to the lower expert id - the order of the ranks above.
+    {
+      constexpr int MAXC = 16;  // candidates per lane: E <= 1024
+      const int C = (E + 63) / 64;
+      for (int t = wave; t < T; t += RT / 64) {
+        const double* zt = s_z + (size_t)t * E;
+        double cz[MAXC];
+        unsigned taken = 0;  // bit j: candidate j is selected or does not exist
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+          const int e = lane + 64 * j;
+          const bool ok = j < C && e < E;
+          cz[j] = ok ? zt[e] : 0.0;
+          taken |= ok ? 0u : 1u << j;
+        }
+        for (int r = 0; r < K; ++r) {
+          double bz = -__builtin_huge_val();
+          int be = 0x7fffffff;  // no candidate: loses to any candidate, also to -inf logits
+#pragma unroll
+          for (int j = 0; j < MAXC; ++j) {
+            const int e = lane + 64 * j;
+            if (!((taken >> j) & 1u) && (cz[j] > bz || (cz[j] == bz && e < be))) {
+              bz = cz[j];
+              be = e;
+            }
+          }
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) {
+            const double oz = __shfl_xor(bz, off);
+            const int oe = __shfl_xor(be, off);
+            if (oz > bz || (oz == bz && oe < be)) {
+              bz = oz;
+              be = oe;
+            }
+          }
+          // every lane holds the winner; its owner marks it taken
+          if ((be & 63) == lane) taken |= 1u << (be >> 6);
+          if (lane == 0) {
+            s_tk_idx[t * K + r] = be;
+            s_tk_z[t * K + r] = bz;
+          }
+        }
       }
     }
   }

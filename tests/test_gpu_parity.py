@@ -151,6 +151,26 @@ def test_decode_rows_longer_than_one_pass(fmt, hidden, tokens, shared):
     _log(f"{wl.name}: max rel-L2 {max(errs):.2e}")
 
 
+@pytest.mark.parametrize("experts,top_k,tokens", [(128, 8, 1), (256, 8, 4), (320, 6, 2)])
+def test_topk_ties_and_expert_counts(experts, top_k, tokens):
+    """Decode top-k with exact ties: every odd expert's router row is a copy of the even
+    expert's before it, so their logits are equal and the lower id must come first.  One token
+    of 128 experts takes the rank-counting top-k; four tokens of 256 and two of 320 (not a
+    multiple of 64) take the wave argmax."""
+    import torch
+    base = mi.WORKLOADS["qwen35b_decode"]
+    wl = dataclasses.replace(base, name=f"ties_e{experts}_k{top_k}_t{tokens}", layers=2,
+                             hidden=256, inter=128, experts=experts, top_k=top_k,
+                             cache_frac=0.5, tokens_per_step=tokens, token_steps=8)
+    _log(f"case {wl.name} C={wl.capacity}")
+    with _bench(wl, groups=0) as wb:
+        wb.router_np[:, 1::2, :] = wb.router_np[:, 0::2, :][:, : experts // 2, :]
+        wb.router.copy_(torch.from_numpy(wb.router_np.view(np.int16)))
+        wb.sync()
+        errs = run_parity(wb, wl.token_steps)
+    _log(f"{wl.name}: max rel-L2 {max(errs):.2e}")
+
+
 @pytest.mark.parametrize("groups", [0, 2])
 def test_mxfp4_four_streams_with_resize(groups):
     """753B-like shape: H 6144, 256 experts top-8, MXFP4, 4 streams per step with cross-request
