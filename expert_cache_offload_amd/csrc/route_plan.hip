@@ -219,7 +219,7 @@ __global__ __launch_bounds__(RT) void route_plan_kernel(RouteArgs a) {
             }
           }
           // every lane holds the winner; its owner marks it taken
-          if ((be & 63) == lane) taken |= 1u << (be >> 6);
+          if (be < E && (be & 63) == lane) taken |= 1u << (be >> 6);  // K <= E: be < E
           if (lane == 0) {
             s_tk_idx[t * K + r] = be;
             s_tk_z[t * K + r] = bz;
